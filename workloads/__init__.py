@@ -1,0 +1,154 @@
+"""Seeded synthetic inputs for the FP8 quantize + block-scaled GEMM path.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests and the
+benchmark.  It holds input generation only: random draws, outlier injection and
+the bf16 storage cast of the inputs.  None of the FP8 method's arithmetic
+(amax, scales, FP8 rounding, GEMM) lives here.
+
+The five workloads mirror the shapes and statistics the pages describe:
+activations ~N(0,1) with a few outlier channels "one or two orders of magnitude
+larger" than the rest (page "Illustrated GPU kernels, Part 8", the outlier
+paragraph after the qdq listing), weights "tightly clustered around zero"
+(page "FP8 Serving", results section 1), and gradient-like data spanning many
+orders of magnitude for the E5M2 operand (page "The FP8 Family", E5M2 row of
+the format table).
+
+Generator recipe (fixed, documented in the design doc as well):
+  rng = numpy.random.default_rng(seed)            # PCG64
+  X   = rng.standard_normal((M, K), float32)
+  if outliers: cols = rng.choice(K, n, replace=False); X[:, cols] *= factor
+  W   = rng.standard_normal((N, K), float32) * 0.02      (normal weights)
+     or sign * 10**rng.uniform(-6, 3, (N, K))            (log-uniform, E5M2)
+  bf16 inputs are the fp32 draws rounded to bf16 (round to nearest even).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+# Enum values shared with include/fp8blk.h (plain integers, no arithmetic).
+E4M3, E5M2 = 0, 1
+GRAN_TENSOR, GRAN_ROW, GRAN_TILE_1x128, GRAN_BLOCK_128x128, GRAN_MX32 = 0, 1, 2, 3, 4
+DT_F32, DT_BF16 = 0, 1
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    M: int
+    N: int
+    K: int
+    in_dtype: int          # DT_F32 or DT_BF16 for both X and W
+    x_fmt: int
+    w_fmt: int
+    x_gran: int
+    w_gran: int
+    out_dtype: int
+    x_outlier_frac: float  # fraction of K-columns that are outliers (0 = none)
+    x_outlier_factor: float
+    w_kind: str            # "normal" (sigma 0.02) or "loguniform" (|w| = 10^U(-6,3))
+    x_outlier_count: Optional[int] = None  # exact count when the page fixes it
+
+    def n_outliers(self, K: Optional[int] = None) -> int:
+        K = self.K if K is None else K
+        if self.x_outlier_count is not None and K == self.K:
+            return self.x_outlier_count
+        return int(round(self.x_outlier_frac * K))
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+# The five configurations of the workload table.
+CONFIGS = {
+    "c1_per_tensor": Workload(
+        "c1_per_tensor", 101, 128, 256, 512, DT_F32, E4M3, E4M3,
+        GRAN_TENSOR, GRAN_TENSOR, DT_F32, 0.0, 50.0, "normal", x_outlier_count=2),
+    "c2_per_token_channel": Workload(
+        "c2_per_token_channel", 102, 2048, 4096, 4096, DT_BF16, E4M3, E4M3,
+        GRAN_ROW, GRAN_ROW, DT_BF16, 0.01, 30.0, "normal"),
+    "c3_deepseek_block": Workload(
+        "c3_deepseek_block", 103, 4096, 7168, 7168, DT_BF16, E4M3, E4M3,
+        GRAN_TILE_1x128, GRAN_BLOCK_128x128, DT_BF16, 0.005, 100.0, "normal"),
+    "c4_decode_skinny": Workload(
+        "c4_decode_skinny", 104, 16, 18432, 7168, DT_BF16, E4M3, E4M3,
+        GRAN_TILE_1x128, GRAN_BLOCK_128x128, DT_BF16, 0.0, 1.0, "normal"),
+    "c5_mxfp8_mix": Workload(
+        "c5_mxfp8_mix", 105, 8192, 8192, 8192, DT_F32, E4M3, E5M2,
+        GRAN_MX32, GRAN_MX32, DT_F32, 0.0, 1.0, "loguniform"),
+}
+
+CONFIG_ORDER = ["c1_per_tensor", "c2_per_token_channel", "c3_deepseek_block",
+                "c4_decode_skinny", "c5_mxfp8_mix"]
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even); returns the uint16 bit patterns.
+
+    Storage cast of the synthetic inputs (finite values only)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bias = ((u >> 16) & 1) + 0x7FFF
+    return ((u + bias) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to fp32 exactly."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def draw_x(wl: Workload, rows: Optional[int] = None, cols: Optional[int] = None,
+           rng: Optional[np.random.Generator] = None) -> np.ndarray:
+    """Activation operand as fp32 values, before the storage cast."""
+    rows = wl.M if rows is None else rows
+    cols = wl.K if cols is None else cols
+    rng = np.random.default_rng(wl.seed) if rng is None else rng
+    x = rng.standard_normal((rows, cols), dtype=np.float32)
+    n = wl.n_outliers(cols)
+    if n > 0:
+        idx = rng.choice(cols, n, replace=False)
+        x[:, idx] *= np.float32(wl.x_outlier_factor)
+    return x
+
+
+def draw_w(wl: Workload, rows: Optional[int] = None, cols: Optional[int] = None,
+           rng: Optional[np.random.Generator] = None) -> np.ndarray:
+    """Weight operand as fp32 values, before the storage cast."""
+    rows = wl.N if rows is None else rows
+    cols = wl.K if cols is None else cols
+    rng = np.random.default_rng(wl.seed + 1000) if rng is None else rng
+    if wl.w_kind == "normal":
+        return rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(0.02)
+    mag = np.power(10.0, rng.uniform(-6.0, 3.0, size=(rows, cols)))
+    sign = np.where(rng.integers(0, 2, size=(rows, cols)) == 1, 1.0, -1.0)
+    return (sign * mag).astype(np.float32)
+
+
+def make_inputs(wl: Workload, M: Optional[int] = None, N: Optional[int] = None,
+                K: Optional[int] = None, seed_offset: int = 0):
+    """Return (x_store, w_store) in the workload's storage dtype.
+
+    fp32 workloads give float32 arrays; bf16 workloads give uint16 bf16 bit
+    patterns.  M/N/K override the shape (for reduced-size parity cases); one
+    generator stream is used so that X is drawn before W.
+    """
+    M = wl.M if M is None else M
+    N = wl.N if N is None else N
+    K = wl.K if K is None else K
+    rng = np.random.default_rng(wl.seed + seed_offset)
+    x = draw_x(wl, M, K, rng)
+    w = draw_w(wl, N, K, rng)
+    if wl.in_dtype == DT_BF16:
+        return f32_to_bf16_bits(x), f32_to_bf16_bits(w)
+    return x, w
+
+
+def storage_to_f32(a: np.ndarray, dtype: int) -> np.ndarray:
+    """Exact fp32 values of a stored operand."""
+    if dtype == DT_BF16:
+        return bf16_bits_to_f32(a)
+    return np.asarray(a, dtype=np.float32)
