@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Throughput of the FP8 quantize + block-scaled GEMM path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input that is
+already resident in HBM:
+    quantize X (bf16 -> E4M3, fp32 scale per 1x128 tile)
+    quantize W (bf16 -> E4M3, fp32 scale per 128x128 block)
+    GEMM  out = sum_kb sX[m,kb] sW[n/128,kb] (X_kb @ W_kb^T), bf16 out
+on the DeepSeek-V3-style block-scaled workload M=4096, N=7168, K=7168.
+`value` is 2*M*N*K / (time per step) in TFLOP/s.  The dominant kernel (the
+GEMM) is also timed on its own with HIP events on the launch stream, and
+reported against the fp8 matrix-core peak; the two quantize kernels are
+reported in algorithmic GB/s against the HBM peak.
+
+Input sets are rotated (R copies, over 1 GB in total) so that no launch
+reads data another launch left in the 256 MB last-level cache.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--copy-probe]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "block-scaled FP8 GEMM TFLOP/s (% fp8 MFMA peak); quantize GB/s (% HBM)"
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 matrix-core peak
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak
+
+
+def scale_bytes(gran: int, rows: int, cols: int) -> int:
+    return {workloads.GRAN_TENSOR: 4, workloads.GRAN_ROW: 4 * rows,
+            workloads.GRAN_TILE_1x128: 4 * rows * (cols // 128),
+            workloads.GRAN_BLOCK_128x128: 4 * (rows // 128) * (cols // 128),
+            workloads.GRAN_MX32: rows * (cols // 32)}[gran]
+
+
+def quant_bytes(wl, operand: str) -> int:
+    """Algorithmic bytes of one quantize: input read once, codes and scales written."""
+    rows, cols = (wl.M, wl.K) if operand == "x" else (wl.N, wl.K)
+    gran = wl.x_gran if operand == "x" else wl.w_gran
+    in_b = 2 if wl.in_dtype == workloads.DT_BF16 else 4
+    return rows * cols * (in_b + 1) + scale_bytes(gran, rows, cols)
+
+
+def gemm_bytes(wl) -> int:
+    """Algorithmic bytes of one GEMM: both code operands and scales read once, output written once."""
+    out_b = 2 if wl.out_dtype == workloads.DT_BF16 else 4
+    return (wl.M * wl.K + wl.N * wl.K + scale_bytes(wl.x_gran, wl.M, wl.K)
+            + scale_bytes(wl.w_gran, wl.N, wl.K) + wl.M * wl.N * out_b)
+
+
+def cpu_baseline(wl, sample_rows: int):
+    """The oracle on the host: quantize a sample of X rows and all of W, then
+    the fp64 GEMM (Ref and the |x||w| bound) of those rows; TFLOP/s of the
+    sample's 2*rows*N*K."""
+    from oracle import gemm as ogemm
+    from oracle import quant as oquant
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    xs, ws = workloads.make_inputs(wl, M=sample_rows)
+    x = workloads.storage_to_f32(xs, wl.in_dtype)
+    w = workloads.storage_to_f32(ws, wl.in_dtype)
+    t0 = time.perf_counter()
+    xq, sx = oquant.quantize(x, wl.x_gran, wl.x_fmt)
+    wq, sw = oquant.quantize(w, wl.w_gran, wl.w_fmt)
+    ref, absb = ogemm.gemm_ref(xq, sx, wl.x_gran, wl.x_fmt, wq, sw, wl.w_gran, wl.w_fmt)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * sample_rows * wl.N * wl.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{sample_rows} of {wl.M} rows of X with all of W: oracle quantize of both operands "
+                      f"plus fp64 GEMM and bound; {dt:.2f} s; numpy BLAS threads={threads}, quantize 1 thread"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3_deepseek_block", choices=workloads.CONFIG_ORDER)
+    ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0 = enough for 1 GB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=256)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 256 MiB device copy (counter calibration for rocprofv3 --pmc)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (sharding is described in "
+              "DESIGN.md); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import block_scaled_precision_x128_amd as fb
+
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        return 1
+    fb.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    if args.copy_probe:
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n}))
+        return 0
+
+    wl = workloads.CONFIGS[args.workload]
+    M, N, K = wl.M, wl.N, wl.K
+    xs_np, ws_np = workloads.make_inputs(wl)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    x0, w0 = to_dev(xs_np), to_dev(ws_np)
+    del xs_np, ws_np
+    in_b = 2 if wl.in_dtype == workloads.DT_BF16 else 4
+    set_bytes = (M + N) * K * (in_b + 1) + M * N * 4
+    R = args.sets or max(2, int(np.ceil(1.2e9 / set_bytes)))
+    sets = []
+    for r in range(R):
+        x = x0 if r == 0 else x0.clone()
+        w = w0 if r == 0 else w0.clone()
+        xq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+        sdt = lambda g: torch.uint8 if g == fb.GRAN_MX32 else torch.float32
+        sx = torch.empty(fb.scale_shape(wl.x_gran, M, K), dtype=sdt(wl.x_gran), device=dev)
+        sw = torch.empty(fb.scale_shape(wl.w_gran, N, K), dtype=sdt(wl.w_gran), device=dev)
+        out = torch.empty((M, N), dtype=torch.bfloat16 if wl.out_dtype == fb.DT_BF16 else torch.float32,
+                          device=dev)
+        sets.append((x, w, xq, wq, sx, sw, out))
+    wsx = torch.empty(max(1, fb.fp8_quantize_workspace_bytes(M, K, wl.x_gran)), dtype=torch.uint8, device=dev)
+    wsw = torch.empty(max(1, fb.fp8_quantize_workspace_bytes(N, K, wl.w_gran)), dtype=torch.uint8, device=dev)
+
+    def step(i, ev=None):
+        x, w, xq, wq, sx, sw, out = sets[i % R]
+        if ev is not None:
+            ev[0].record(stream)
+        fb.fp8_quantize(x, wl.x_fmt, wl.x_gran, q=xq, scales=sx, workspace=wsx, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fb.fp8_quantize(w, wl.w_fmt, wl.w_gran, q=wq, scales=sw, workspace=wsw, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        fb.fp8_gemm_blockscaled(xq, wl.x_fmt, wl.x_gran, sx, wq, wl.w_fmt, wl.w_gran, sw, wl.out_dtype,
+                                out=out, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: whole steps, bracketed by synchronizations
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    qx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    qw_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    gm_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    flops = 2.0 * M * N * K
+    value = flops / (ms_step * 1e-3) / 1e12
+    gemm_tflops = flops / (gm_ms * 1e-3) / 1e12
+    qx_gbs = quant_bytes(wl, "x") / (qx_ms * 1e-3) / 1e9
+    qw_gbs = quant_bytes(wl, "w") / (qw_ms * 1e-3) / 1e9
+    gemm_hbm_gbs = gemm_bytes(wl) / (gm_ms * 1e-3) / 1e9
+
+    skinny = wl.M <= 32
+    if skinny:
+        roof = {"bound": "hbm", "achieved": round(gemm_hbm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gemm_hbm_gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "traffic": None}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 x fp8_e4m3 -> f32 accumulate",
+        "data": "synthetic (seeded; bf16 activations ~N(0,1) with outlier channels, weights ~N(0,0.02))",
+        "config": {"workload": f"{wl.name}: M={M} N={N} K={K}, X 1x128 tiles, W 128x128 blocks, "
+                               f"E4M3, fp32 scales, bf16 out" if wl.name == "c3_deepseek_block" else
+                               f"{wl.name}: M={M} N={N} K={K}",
+                   "step": "quantize X + quantize W + GEMM", "rotated_input_sets": R},
+        "roofline": roof,
+        "kernels": {
+            "gemm_ms": round(gm_ms, 4), "gemm_tflops": round(gemm_tflops, 1),
+            "gemm_frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+            "gemm_algorithmic_gbs": round(gemm_hbm_gbs, 1),
+            "quantize_x_ms": round(qx_ms, 4), "quantize_x_gbs": round(qx_gbs, 1),
+            "quantize_x_frac_hbm": round(qx_gbs / PEAK_HBM_GBS, 4),
+            "quantize_w_ms": round(qw_ms, 4), "quantize_w_gbs": round(qw_gbs, 1),
+            "quantize_w_frac_hbm": round(qw_gbs / PEAK_HBM_GBS, 4),
+        },
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_sample_rows, M))
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

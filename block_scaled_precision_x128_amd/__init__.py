@@ -1,0 +1,201 @@
+"""Python binding of libfp8blk, the MI355X (gfx950) FP8 quantize + block-scaled
+FP8 GEMM library.
+
+The functions mirror the C ABI in include/fp8blk.h by name.  They only marshal
+arguments: torch tensors supply device memory and the current HIP stream, every
+step of the computation runs in the library's HIP kernels.  When the library
+is missing or no GPU is present, every call raises; there is no CPU fallback.
+
+Enum values (same as the C header):
+  formats        E4M3 = 0, E5M2 = 1
+  granularities  GRAN_TENSOR = 0, GRAN_ROW = 1, GRAN_TILE_1x128 = 2,
+                 GRAN_BLOCK_128x128 = 3, GRAN_MX32 = 4
+  dtypes         DT_F32 = 0, DT_BF16 = 1
+  GEMM kernels   GEMM_AUTO = 0, GEMM_TILED = 1, GEMM_SKINNY = 2
+  accumulation   ACCUM_FP32 = 0 (exact products, fp32 sums), ACCUM_NATIVE = 1
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+E4M3, E5M2 = 0, 1
+GRAN_TENSOR, GRAN_ROW, GRAN_TILE_1x128, GRAN_BLOCK_128x128, GRAN_MX32 = 0, 1, 2, 3, 4
+DT_F32, DT_BF16 = 0, 1
+GEMM_AUTO, GEMM_TILED, GEMM_SKINNY = 0, 1, 2
+ACCUM_FP32, ACCUM_NATIVE = 0, 1
+
+FP8_OK = 0
+STATUS_NAMES = {0: "FP8_OK", 1: "FP8_ERR_NULL", 2: "FP8_ERR_ENUM", 3: "FP8_ERR_SHAPE",
+                4: "FP8_ERR_UNSUPPORTED", 5: "FP8_ERR_WORKSPACE", 6: "FP8_ERR_HIP", 7: "FP8_ERR_ALIGN"}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8blk.so")
+
+# Exported symbols and their C signatures (include/fp8blk.h).
+_c = ctypes
+_SIGS = {
+    "fp8_status_string": (_c.c_char_p, [_c.c_int]),
+    "fp8_abi_version": (_c.c_int, []),
+    "fp8_quantize_workspace_bytes": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int]),
+    "fp8_quantize": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int, _c.c_int,
+                                _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "fp8_dequantize": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int, _c.c_int,
+                                  _c.c_void_p, _c.c_int, _c.c_void_p]),
+    "fp8_cast": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_void_p]),
+    "fp8_gemm_blockscaled": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_void_p,
+                                        _c.c_void_p, _c.c_int, _c.c_int, _c.c_void_p,
+                                        _c.c_int64, _c.c_int64, _c.c_int64,
+                                        _c.c_void_p, _c.c_int, _c.c_void_p]),
+    "fp8_gemm_blockscaled_ex": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_void_p,
+                                           _c.c_void_p, _c.c_int, _c.c_int, _c.c_void_p,
+                                           _c.c_int64, _c.c_int64, _c.c_int64,
+                                           _c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_void_p]),
+}
+EXPORTS = tuple(_SIGS)
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class Fp8Error(RuntimeError):
+    """A libfp8blk call returned a non-OK status."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {STATUS_NAMES.get(status, status)} ({msg})")
+        self.status = status
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libfp8blk.so (built by build.py) and declare its signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libfp8blk.so not found at {p}: build it with "
+                           "`python -m block_scaled_precision_x128_amd.build` (there is no fallback)")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGS.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(fn: str, st: int):
+    if st != FP8_OK:
+        raise Fp8Error(fn, st, load_library().fp8_status_string(st).decode())
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("libfp8blk needs a ROCm GPU; torch.cuda.is_available() is False")
+    return torch
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _dt_of(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DT_F32
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _torch_dtype(dt: int):
+    torch = _torch()
+    return torch.float32 if dt == DT_F32 else torch.bfloat16
+
+
+def scale_shape(gran: int, rows: int, cols: int):
+    return {GRAN_TENSOR: (1,), GRAN_ROW: (rows,), GRAN_TILE_1x128: (rows, cols // 128),
+            GRAN_BLOCK_128x128: (rows // 128, cols // 128), GRAN_MX32: (rows, cols // 32)}[gran]
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+# ---- raw entry points (pointers and sizes, as in C) -------------------------
+
+def fp8_status_string(status: int) -> str:
+    return load_library().fp8_status_string(status).decode()
+
+
+def fp8_abi_version() -> int:
+    return load_library().fp8_abi_version()
+
+
+def fp8_quantize_workspace_bytes(rows: int, cols: int, gran: int) -> int:
+    return load_library().fp8_quantize_workspace_bytes(rows, cols, gran)
+
+
+# ---- tensor-level wrappers ----------------------------------------------------
+
+def fp8_quantize(x, fmt: int, gran: int, q=None, scales=None, workspace=None, stream=None):
+    """Quantize a 2-D fp32/bf16 device tensor.  Returns (codes uint8, scales)."""
+    torch = _torch()
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        sdt = torch.uint8 if gran == GRAN_MX32 else torch.float32
+        scales = torch.empty(scale_shape(gran, rows, cols), dtype=sdt, device=x.device)
+    lib = load_library()
+    ws = lib.fp8_quantize_workspace_bytes(rows, cols, gran)
+    if ws and workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.fp8_quantize(x.data_ptr(), _dt_of(x), rows, cols, fmt, gran, q.data_ptr(), scales.data_ptr(),
+                          _ptr(workspace), wsb, _stream(stream))
+    _check("fp8_quantize", st)
+    return q, scales
+
+
+def fp8_dequantize(q, scales, fmt: int, gran: int, out_dtype: int = DT_F32, y=None, stream=None):
+    """Dequantize codes to fp32 or bf16.  Returns y."""
+    torch = _torch()
+    rows, cols = q.shape
+    if y is None:
+        y = torch.empty((rows, cols), dtype=_torch_dtype(out_dtype), device=q.device)
+    st = load_library().fp8_dequantize(q.data_ptr(), scales.data_ptr(), rows, cols, fmt, gran, y.data_ptr(),
+                                       out_dtype, _stream(stream))
+    _check("fp8_dequantize", st)
+    return y
+
+
+def fp8_cast(x, fmt: int, q=None, stream=None):
+    """Unscaled saturating cast of a fp32/bf16 device tensor (numel % 8 == 0)."""
+    torch = _torch()
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    st = load_library().fp8_cast(x.data_ptr(), _dt_of(x), x.numel(), fmt, q.data_ptr(), _stream(stream))
+    _check("fp8_cast", st)
+    return q
+
+
+def fp8_gemm_blockscaled(a, a_fmt: int, a_gran: int, a_scales, b, b_fmt: int, b_gran: int, b_scales,
+                         out_dtype: int = DT_BF16, out=None, algo: int = GEMM_AUTO, accum: int = ACCUM_FP32,
+                         stream=None):
+    """out[M, N] = (a * sA) @ (b * sB)^T for codes a [M, K], b [N, K]."""
+    torch = _torch()
+    M, K = a.shape
+    N = b.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=_torch_dtype(out_dtype), device=a.device)
+    st = load_library().fp8_gemm_blockscaled_ex(
+        a.data_ptr(), a_fmt, a_gran, a_scales.data_ptr(), b.data_ptr(), b_fmt, b_gran, b_scales.data_ptr(),
+        M, N, K, out.data_ptr(), out_dtype, algo, accum, _stream(stream))
+    _check("fp8_gemm_blockscaled", st)
+    return out

@@ -1,0 +1,163 @@
+// C ABI of libfp8blk: argument validation on the host, then kernel selection
+// and launch on the caller's stream.  Declarations and the meaning of every
+// argument are in include/fp8blk.h.
+#include "../../include/fp8blk.h"
+
+#include <limits.h>
+
+#include "kernels.h"
+
+using namespace fp8blk;
+
+namespace {
+
+bool valid_fmt(fp8_format_t f) { return f == FP8_E4M3 || f == FP8_E5M2; }
+bool valid_dt(fp8_dtype_t d) { return d == FP8_DT_F32 || d == FP8_DT_BF16; }
+bool valid_gran(fp8_granularity_t g) { return g >= FP8_GRAN_TENSOR && g <= FP8_GRAN_MX32; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Product of two non-negative sizes, or -1 if it overflows.
+int64_t mul_checked(int64_t a, int64_t b) {
+  if (a == 0 || b == 0) return 0;
+  if (a > INT64_MAX / b) return -1;
+  return a * b;
+}
+
+fp8_status_t check_operand(int64_t rows, int64_t cols, fp8_granularity_t g) {
+  if (rows < 0 || cols < 0) return FP8_ERR_SHAPE;
+  if (cols % 128 != 0) return FP8_ERR_SHAPE;
+  if (g == FP8_GRAN_BLOCK_128x128 && rows % 128 != 0) return FP8_ERR_SHAPE;
+  const int64_t total = mul_checked(rows, cols);
+  if (total < 0) return FP8_ERR_SHAPE;
+  // every launch below keeps its grid under 2^31 workgroups
+  if (total / 32 / 256 >= INT_MAX || rows >= INT_MAX) return FP8_ERR_SHAPE;
+  return FP8_OK;
+}
+
+fp8_status_t hip_status(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8_status_string(fp8_status_t st) {
+  switch (st) {
+    case FP8_OK: return "ok";
+    case FP8_ERR_NULL: return "a required pointer is NULL";
+    case FP8_ERR_ENUM: return "invalid format, granularity, dtype or algorithm value";
+    case FP8_ERR_SHAPE: return "invalid shape (negative, K % 128, rows % 128 for 128x128 blocks, M/N % 16, or too large)";
+    case FP8_ERR_UNSUPPORTED: return "unsupported combination";
+    case FP8_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP8_ERR_HIP: return "HIP launch failed";
+    case FP8_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, fp32 scales 4 bytes)";
+  }
+  return "unknown status";
+}
+
+int fp8_abi_version(void) { return FP8BLK_ABI_VERSION; }
+
+size_t fp8_quantize_workspace_bytes(int64_t rows, int64_t cols, fp8_granularity_t g) {
+  if (!valid_gran(g) || check_operand(rows, cols, g) != FP8_OK) return 0;
+  return g == FP8_GRAN_TENSOR ? sizeof(float) * (size_t)kTensorPartials : 0;
+}
+
+fp8_status_t fp8_quantize(const void* x, fp8_dtype_t x_dt, int64_t rows, int64_t cols, fp8_format_t fmt,
+                          fp8_granularity_t g, uint8_t* q, void* scales, void* workspace, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (!valid_dt(x_dt) || !valid_fmt(fmt) || !valid_gran(g)) return FP8_ERR_ENUM;
+  const fp8_status_t sh = check_operand(rows, cols, g);
+  if (sh != FP8_OK) return sh;
+  const int64_t total = rows * cols;
+  if (total > 0 && (!x || !q)) return FP8_ERR_NULL;
+  if ((total > 0 || g == FP8_GRAN_TENSOR) && !scales) return FP8_ERR_NULL;
+  if (total > 0 && (!aligned(x, 16) || !aligned(q, 16))) return FP8_ERR_ALIGN;
+  if (g != FP8_GRAN_MX32 && scales && !aligned(scales, 4)) return FP8_ERR_ALIGN;
+  if (g == FP8_GRAN_TENSOR && total > 0) {
+    if (!workspace || ws_bytes < sizeof(float) * (size_t)kTensorPartials) return FP8_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return FP8_ERR_ALIGN;
+  }
+  return hip_status(launch_quantize(x, (int)x_dt, rows, cols, (int)fmt, (int)g, q, scales, workspace, stream));
+}
+
+fp8_status_t fp8_dequantize(const uint8_t* q, const void* scales, int64_t rows, int64_t cols, fp8_format_t fmt,
+                            fp8_granularity_t g, void* y, fp8_dtype_t y_dt, hipStream_t stream) {
+  if (!valid_dt(y_dt) || !valid_fmt(fmt) || !valid_gran(g)) return FP8_ERR_ENUM;
+  const fp8_status_t sh = check_operand(rows, cols, g);
+  if (sh != FP8_OK) return sh;
+  const int64_t total = rows * cols;
+  if (total == 0) return FP8_OK;
+  if (!q || !scales || !y) return FP8_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(y, 16)) return FP8_ERR_ALIGN;
+  if (g != FP8_GRAN_MX32 && !aligned(scales, 4)) return FP8_ERR_ALIGN;
+  return hip_status(launch_dequantize(q, scales, rows, cols, (int)fmt, (int)g, y, (int)y_dt, stream));
+}
+
+fp8_status_t fp8_cast(const void* x, fp8_dtype_t x_dt, int64_t n, fp8_format_t fmt, uint8_t* q,
+                      hipStream_t stream) {
+  if (!valid_dt(x_dt) || !valid_fmt(fmt)) return FP8_ERR_ENUM;
+  if (n < 0 || n % 8 != 0 || n / 8 / 256 >= INT_MAX) return FP8_ERR_SHAPE;
+  if (n == 0) return FP8_OK;
+  if (!x || !q) return FP8_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 8)) return FP8_ERR_ALIGN;
+  return hip_status(launch_cast(x, (int)x_dt, n, (int)fmt, q, stream));
+}
+
+fp8_status_t fp8_gemm_blockscaled_ex(const uint8_t* a, fp8_format_t a_fmt, fp8_granularity_t a_g,
+                                     const void* a_scales, const uint8_t* b, fp8_format_t b_fmt,
+                                     fp8_granularity_t b_g, const void* b_scales, int64_t M, int64_t N, int64_t K,
+                                     void* out, fp8_dtype_t out_dt, fp8_gemm_algo_t algo, fp8_accum_t accum,
+                                     hipStream_t stream) {
+  if (!valid_fmt(a_fmt) || !valid_fmt(b_fmt) || !valid_gran(a_g) || !valid_gran(b_g) || !valid_dt(out_dt))
+    return FP8_ERR_ENUM;
+  if (algo != FP8_GEMM_AUTO && algo != FP8_GEMM_TILED && algo != FP8_GEMM_SKINNY) return FP8_ERR_ENUM;
+  if (accum != FP8_ACCUM_FP32 && accum != FP8_ACCUM_NATIVE) return FP8_ERR_ENUM;
+  if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 128) return FP8_ERR_SHAPE;
+  if (mul_checked(M, K) < 0 || mul_checked(N, K) < 0 || mul_checked(M, N) < 0) return FP8_ERR_SHAPE;
+  if ((M / 128 + 1) * (N / 128 + 1) >= INT_MAX || N / 16 >= INT_MAX) return FP8_ERR_SHAPE;
+
+  int mode;
+  const bool a_tr = (a_g == FP8_GRAN_TENSOR || a_g == FP8_GRAN_ROW);
+  const bool b_tr = (b_g == FP8_GRAN_TENSOR || b_g == FP8_GRAN_ROW);
+  if (a_tr && b_tr) mode = MODE_EPILOGUE;
+  else if (a_g == FP8_GRAN_TILE_1x128 && b_g == FP8_GRAN_BLOCK_128x128) mode = MODE_PROMOTE;
+  else if (a_g == FP8_GRAN_MX32 && b_g == FP8_GRAN_MX32) mode = MODE_MX;
+  else return FP8_ERR_UNSUPPORTED;
+  if (b_g == FP8_GRAN_BLOCK_128x128 && N % 128) return FP8_ERR_SHAPE;
+  if (algo == FP8_GEMM_SKINNY && M > 64) return FP8_ERR_UNSUPPORTED;
+
+  if (M == 0 || N == 0) return FP8_OK;
+  if (!out) return FP8_ERR_NULL;
+  if (!aligned(out, 16)) return FP8_ERR_ALIGN;
+  const int64_t out_bytes = M * N * (out_dt == FP8_DT_F32 ? 4 : 2);
+  if (K == 0) return hip_status(launch_fill_zero(out, out_bytes, stream));
+  if (!a || !b || !a_scales || !b_scales) return FP8_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b, 16)) return FP8_ERR_ALIGN;
+  // fp32 scales are read as floats; UE8M0 scales as 4-byte words (4 blocks of 32)
+  if (!aligned(a_scales, 4) || !aligned(b_scales, 4)) return FP8_ERR_ALIGN;
+
+  GemmArgs p;
+  p.a = a;
+  p.b = b;
+  p.sa = a_scales;
+  p.sb = b_scales;
+  p.out = out;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.a_per_row = (a_g == FP8_GRAN_ROW);
+  p.b_per_row = (b_g == FP8_GRAN_ROW);
+  const int path = accum == FP8_ACCUM_NATIVE ? PATH_FAST : PATH_EXACT;
+  const bool skinny = (algo == FP8_GEMM_SKINNY) || (algo == FP8_GEMM_AUTO && M <= 32);
+  if (skinny) return hip_status(launch_gemm_skinny(p, (int)a_fmt, (int)b_fmt, mode, (int)out_dt, path, stream));
+  return hip_status(launch_gemm_tiled(p, (int)a_fmt, (int)b_fmt, mode, (int)out_dt, path, stream));
+}
+
+fp8_status_t fp8_gemm_blockscaled(const uint8_t* a, fp8_format_t a_fmt, fp8_granularity_t a_g,
+                                  const void* a_scales, const uint8_t* b, fp8_format_t b_fmt,
+                                  fp8_granularity_t b_g, const void* b_scales, int64_t M, int64_t N, int64_t K,
+                                  void* out, fp8_dtype_t out_dt, hipStream_t stream) {
+  return fp8_gemm_blockscaled_ex(a, a_fmt, a_g, a_scales, b, b_fmt, b_g, b_scales, M, N, K, out, out_dt,
+                                 FP8_GEMM_AUTO, FP8_ACCUM_FP32, stream);
+}
+
+}  // extern "C"

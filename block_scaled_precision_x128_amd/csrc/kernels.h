@@ -1,0 +1,39 @@
+// Internal launcher interface of libfp8blk (host side, C++ linkage).  The
+// public C ABI in include/fp8blk.h validates arguments and calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8blk {
+
+// Number of per-workgroup partial maxima of the per-tensor amax pass; the
+// per-tensor quantize needs kTensorPartials floats of workspace.
+constexpr int kTensorPartials = 1024;
+
+enum { MODE_EPILOGUE = 0, MODE_PROMOTE = 1, MODE_MX = 2 };
+// Matrix-core path: exact products with fp32 sums (bf16 instructions on the
+// expanded codes), or the FP8 instructions' own accumulation.
+enum { PATH_EXACT = 0, PATH_FAST = 1 };
+
+struct GemmArgs {
+  const uint8_t* a;   // [M, K] codes
+  const uint8_t* b;   // [N, K] codes
+  const void* sa;     // scales of a (layout per granularity)
+  const void* sb;     // scales of b
+  void* out;          // [M, N]
+  int64_t M, N, K;
+  int a_per_row;      // epilogue mode: 1 = one scale per row of a, 0 = one per tensor
+  int b_per_row;      // epilogue mode: same for b
+};
+
+hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, int fmt, int g, uint8_t* q,
+                           void* scales, void* ws, hipStream_t st);
+hipError_t launch_cast(const void* x, int dt, int64_t n, int fmt, uint8_t* q, hipStream_t st);
+hipError_t launch_dequantize(const uint8_t* q, const void* scales, int64_t rows, int64_t cols, int fmt, int g,
+                             void* y, int odt, hipStream_t st);
+hipError_t launch_gemm_tiled(const GemmArgs& p, int afmt, int bfmt, int mode, int odt, int path, hipStream_t st);
+hipError_t launch_gemm_skinny(const GemmArgs& p, int afmt, int bfmt, int mode, int odt, int path, hipStream_t st);
+hipError_t launch_fill_zero(void* out, int64_t bytes, hipStream_t st);
+
+}  // namespace fp8blk

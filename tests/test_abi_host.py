@@ -1,0 +1,112 @@
+"""The C-ABI library on the host: it loads, exports every function the header
+declares, and rejects bad arguments with status codes before touching HIP
+(so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_precision_x128_amd as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8blk.h")
+
+
+def _ensure_built():
+    if not os.path.exists(fb.LIB_PATH):
+        from block_scaled_precision_x128_amd import build
+        build.build()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**(fp8_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    _ensure_built()
+    return fb.load_library()
+
+
+def test_header_declares_the_binding_exports():
+    assert header_functions() == sorted(fb.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert lib.fp8_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for st in range(8):
+        assert lib.fp8_status_string(st)
+    assert lib.fp8_status_string(99) == b"unknown status"
+
+
+def test_workspace_query(lib):
+    assert lib.fp8_quantize_workspace_bytes(128, 512, fb.GRAN_TENSOR) == 4096
+    for g in (fb.GRAN_ROW, fb.GRAN_TILE_1x128, fb.GRAN_BLOCK_128x128, fb.GRAN_MX32):
+        assert lib.fp8_quantize_workspace_bytes(128, 512, g) == 0
+    assert lib.fp8_quantize_workspace_bytes(128, 500, fb.GRAN_TENSOR) == 0
+
+
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced by these calls
+
+
+def test_quantize_validation(lib):
+    q = lib.fp8_quantize
+    assert q(FAKE, 0, 4, 128, 5, fb.GRAN_ROW, FAKE, FAKE, None, 0, None) == 2          # bad format
+    assert q(FAKE, 7, 4, 128, 0, fb.GRAN_ROW, FAKE, FAKE, None, 0, None) == 2          # bad dtype
+    assert q(FAKE, 0, 4, 128, 0, 9, FAKE, FAKE, None, 0, None) == 2                    # bad granularity
+    assert q(FAKE, 0, 4, 100, 0, fb.GRAN_ROW, FAKE, FAKE, None, 0, None) == 3          # K % 128
+    assert q(FAKE, 0, -1, 128, 0, fb.GRAN_ROW, FAKE, FAKE, None, 0, None) == 3         # negative
+    assert q(FAKE, 0, 100, 128, 0, fb.GRAN_BLOCK_128x128, FAKE, FAKE, None, 0, None) == 3
+    assert q(None, 0, 4, 128, 0, fb.GRAN_ROW, FAKE, FAKE, None, 0, None) == 1          # null x
+    assert q(FAKE, 0, 4, 128, 0, fb.GRAN_ROW, FAKE, None, None, 0, None) == 1          # null scales
+    assert q(FAKE + 8, 0, 4, 128, 0, fb.GRAN_ROW, FAKE, FAKE, None, 0, None) == 7      # misaligned x
+    assert q(FAKE, 0, 4, 128, 0, fb.GRAN_ROW, FAKE, FAKE + 2, None, 0, None) == 7      # misaligned scales
+    assert q(FAKE, 0, 4, 128, 0, fb.GRAN_TENSOR, FAKE, FAKE, None, 0, None) == 5       # no workspace
+    assert q(FAKE, 0, 4, 128, 0, fb.GRAN_TENSOR, FAKE, FAKE, FAKE, 100, None) == 5     # small workspace
+    assert q(FAKE, 0, 2 ** 62, 2 ** 20, 0, fb.GRAN_ROW, FAKE, FAKE, None, 0, None) == 3  # overflow
+    # empty input with a non-tensor granularity is a no-op that needs no pointers
+    assert q(None, 0, 0, 128, 0, fb.GRAN_ROW, None, None, None, 0, None) == 0
+
+
+def test_dequantize_and_cast_validation(lib):
+    d = lib.fp8_dequantize
+    assert d(FAKE, FAKE, 4, 128, 3, 0, FAKE, 0, None) == 2
+    assert d(FAKE, FAKE, 4, 120, 0, 0, FAKE, 0, None) == 3
+    assert d(None, FAKE, 4, 128, 0, 0, FAKE, 0, None) == 1
+    assert d(FAKE, FAKE, 4, 128, 0, 0, FAKE + 4, 0, None) == 7
+    assert d(None, None, 0, 128, 0, 0, None, 0, None) == 0
+    c = lib.fp8_cast
+    assert c(FAKE, 0, 12, 0, FAKE, None) == 3
+    assert c(FAKE, 0, 16, 2, FAKE, None) == 2
+    assert c(None, 0, 16, 0, FAKE, None) == 1
+    assert c(None, 0, 0, 0, None, None) == 0
+
+
+def test_gemm_validation(lib):
+    g = lib.fp8_gemm_blockscaled_ex
+    T, R, TL, BL, MX = (fb.GRAN_TENSOR, fb.GRAN_ROW, fb.GRAN_TILE_1x128, fb.GRAN_BLOCK_128x128, fb.GRAN_MX32)
+    args = lambda ag, bg, M=32, N=128, K=256, out=FAKE, algo=0, a=FAKE, od=1, acc=0: (
+        a, 0, ag, FAKE, FAKE, 0, bg, FAKE, M, N, K, out, od, algo, acc, None)
+    assert g(*args(TL, TL)) == 4             # unsupported pair
+    assert g(*args(MX, T)) == 4
+    assert g(*args(BL, BL)) == 4
+    assert g(*args(T, T, M=24)) == 3         # M % 16
+    assert g(*args(T, T, K=200)) == 3        # K % 128
+    assert g(*args(TL, BL, N=144)) == 3      # 128x128 blocks need N % 128
+    assert g(*args(T, T, algo=5)) == 2
+    assert g(*args(T, T, M=128, algo=fb.GEMM_SKINNY)) == 4
+    assert g(*args(T, T, a=None)) == 1
+    assert g(*args(T, T, out=None)) == 1
+    assert g(*args(T, T, a=FAKE + 1)) == 7
+    assert g(*args(T, T, od=3)) == 2
+    assert g(*args(T, T, acc=2)) == 2
+    assert g(*args(T, T, M=0)) == 0          # empty output: nothing to do
