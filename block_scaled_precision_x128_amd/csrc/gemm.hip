@@ -108,10 +108,21 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel: 128x128 output tile per workgroup, 4 waves of 64x64, 128-K
-// steps, double-buffered LDS fed through registers.
+// Tiled kernel: 256x256 output tile per workgroup of 8 waves (2 along M x 4
+// along N, 128x64 each), 128-K steps.  Both operand tiles are FP8 in LDS,
+// double-buffered; global data goes to LDS with buffer_load ... lds (no
+// register staging), through descriptors that cover only the tile's valid
+// rows, so rows past M or N arrive as zeros.  One barrier per K step: the
+// loads of step k+1 are issued right after it and land while step k computes.
+//
+// LDS tile layout: 128-byte rows of eight 16-byte chunks; chunk c of row r is
+// stored at chunk c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment
+// read has each 16-lane group fetch one chunk from each of 16 consecutive
+// rows; with this swizzle those reads are free of LDS bank conflicts on
+// gfx950 (measured with SQ_LDS_BANK_CONFLICT; the plain r & 7 and (r >> 1) & 7
+// swizzles both stall 4 cycles per ds_read_b128).
 // ---------------------------------------------------------------------------
-constexpr int TBM = 128, TBN = 128, TBK = 128;
+constexpr int TBK = 128;
 
 // Workgroup id -> output tile.  Consecutive ids are dispatched round-robin
 // over the 8 XCDs; each XCD is given a contiguous run of logical tiles, and
@@ -132,192 +143,227 @@ __device__ __forceinline__ void tile_coords(int64_t bid, int64_t ntm, int64_t nt
   tn = in_g / gm;
 }
 
-template <int AF, int BF, int MODE, int ODT, int PATH>
-__global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][(TBM + TBN) * TBK];
-  __shared__ __attribute__((aligned(16))) float s_x[2][TBM];           // MODE_PROMOTE: sA[m, kb]
-  __shared__ __attribute__((aligned(16))) uint32_t s_e[2][TBM + TBN];  // MODE_MX: 4 scale bytes per row
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Chunk swizzle of LDS tile row r (see the layout note above).
+__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int AF, int BF, int MODE, int ODT, int PATH, int WMW, int WNW>
+__device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
+  constexpr int TBM = 128 * WMW, TBN = 64 * WNW;       // workgroup tile
+  constexpr int NW = WMW * WNW;                        // waves
+  constexpr int LPW = (TBM + TBN) / 8 / NW;            // 1-KiB loads per wave per K step
+  static_assert((TBM + TBN) % (8 * NW) == 0, "rows must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][(TBM + TBN) * TBK];
+  __shared__ __attribute__((aligned(16))) float s_x[2][TBM];                     // MODE_PROMOTE: sA[m, kb]
+  __shared__ __attribute__((aligned(16))) uint32_t s_e[2][TBM + TBN];            // MODE_MX: 4 scale bytes per row
 
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t ntm = (M + TBM - 1) / TBM, ntn = (N + TBN - 1) / TBN;
   int64_t tm, tn;
   tile_coords(blockIdx.x, ntm, ntn, tm, tn);
   const int64_t m0 = tm * TBM, n0 = tn * TBN;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = w / WNW, wn = w % WNW;  // wave tile: rows wm*128.., cols wn*64..
   const int nkb = (int)(K / 128);
-
-  // global -> LDS: thread t moves 16-byte chunk (t & 7) of rows (t >> 3) + 32 i.
-  // LDS rows are 128 bytes; chunk c of row r is stored at chunk c ^ (r & 7).
-  // Global reads go through buffer descriptors that start at the tile's first
-  // row and cover only its valid rows: rows past M (or N) read as zero.
-  const int lr = t >> 3, lc = t & 7;
   const int64_t rows_a = (M - m0) < TBM ? (M - m0) : TBM;
   const int64_t rows_b = (N - n0) < TBN ? (N - n0) : TBN;
+
+  // Operand descriptors start at the tile's first row and end after its last valid row.
   const __amdgpu_buffer_rsrc_t rsa =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a + m0 * K), 0, (int)(rows_a * K), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsb =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.b + n0 * K), 0, (int)(rows_b * K), kBufferFlags);
-  const int goff = lr * (int)K + lc * 16;   // byte offset of this thread's chunk in row lr
-  const int rstep = 32 * (int)K;            // 32 rows
-  int loff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lr + 32 * i;
-    loff[i] = r * 128 + ((lc ^ (r & 7)) << 4);
+  // The TBM A rows and TBN B rows of a K step form one list of LDS rows,
+  // 8 rows (1 KiB) per load instruction; wave w issues instructions
+  // [w*LPW, w*LPW + LPW).  Lane q lands in row 8u + q/8, stored chunk q%8,
+  // which holds logical chunk (q%8) ^ lds_swz(row).
+  // Row 8x + q/8 has lds_swz = (q/8) ^ (x & 1), so a lane's offset is one of
+  // two per-lane values plus a wave-uniform row shift.
+  const int q8 = lane >> 3;
+  const int goff_even = q8 * (int)K + (((lane & 7) ^ q8) << 4);
+  const int goff_odd = q8 * (int)K + (((lane & 7) ^ q8 ^ 1) << 4);
+  auto goff = [&](int x) {           // x: 8-row block index inside its own tile
+    return ((x & 1) ? goff_odd : goff_even) + 8 * x * (int)K;
+  };
+
+  // Scale descriptors (same row ranges) and per-lane offsets of the staged scales.
+  const int64_t kq = K / 32;
+  __amdgpu_buffer_rsrc_t rssa = rsa, rssb = rsb;
+  if constexpr (MODE == MODE_PROMOTE)
+    rssa = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(reinterpret_cast<const float*>(p.sa) + m0 * nkb), 0,
+                                             (int)(rows_a * nkb * 4), kBufferFlags);
+  if constexpr (MODE == MODE_MX) {
+    rssa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.sa) + m0 * kq), 0,
+                                             (int)(rows_a * kq), kBufferFlags);
+    rssb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.sb) + n0 * kq), 0,
+                                             (int)(rows_b * kq), kBufferFlags);
   }
-  const float* sxa = reinterpret_cast<const float*>(p.sa);
   const float* swb = reinterpret_cast<const float*>(p.sb);
-  const uint8_t* eab = reinterpret_cast<const uint8_t*>(p.sa);
-  const uint8_t* ebb = reinterpret_cast<const uint8_t*>(p.sb);
-  const int64_t srow_a = (m0 + (t & 127) < M) ? m0 + (t & 127) : M - 1;
-  const int64_t srow_b = (n0 + (t & 127) < N) ? n0 + (t & 127) : N - 1;
+  const float* sxa = reinterpret_cast<const float*>(p.sa);
 
-  u32x4 ra[4], rb[4];
-  float rsx = 0.0f;
-  uint32_t re = 0;
-
-  auto gload = [&](int kb) {
+  auto issue_loads = [&](int kb, int buf) {
     const int kk = kb * 128;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = buffer_load16(rsa, goff + i * rstep + kk);
-      rb[i] = buffer_load16(rsb, goff + i * rstep + kk);
+    for (int u = 0; u < LPW; ++u) {
+      const int x = w * LPW + u;       // 8-row block of the A+B list (wave-uniform)
+      if (8 * x < TBM)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, LDS_PTR(&smem[buf][8 * x * 128]), 16, goff(x) + kk, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, LDS_PTR(&smem[buf][8 * x * 128]), 16, goff(x - TBM / 8) + kk,
+                                                 0, 0, 0);
     }
+    // scales: one 4-byte load per lane, 64 rows per wave; A rows first, then B rows (MX)
     if constexpr (MODE == MODE_PROMOTE) {
-      if (t < TBM) rsx = sxa[srow_a * nkb + kb];
+#pragma unroll
+      for (int v = w; v < TBM / 64; v += NW)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rssa, LDS_PTR(&s_x[buf][64 * v]), 4, ((64 * v + lane) * nkb + kb) * 4,
+                                                 0, 0, 0);
     }
     if constexpr (MODE == MODE_MX) {
-      const int64_t kq = K / 32;
-      if (t < TBM) re = *reinterpret_cast<const uint32_t*>(eab + srow_a * kq + kb * 4);
-      else re = *reinterpret_cast<const uint32_t*>(ebb + srow_b * kq + kb * 4);
-    }
-  };
-  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(&smem[buf][loff[i]]) = ra[i];
-      *reinterpret_cast<u32x4*>(&smem[buf][TBM * TBK + loff[i]]) = rb[i];
+      for (int v = w; v < (TBM + TBN) / 64; v += NW) {
+        if (v < TBM / 64)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rssa, LDS_PTR(&s_e[buf][64 * v]), 4,
+                                                   (int)((64 * v + lane) * kq + kb * 4), 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rssb, LDS_PTR(&s_e[buf][64 * v]), 4,
+                                                   (int)((64 * v - TBM + lane) * kq + kb * 4), 0, 0, 0);
+      }
     }
-    if constexpr (MODE == MODE_PROMOTE) {
-      if (t < TBM) s_x[buf][t] = rsx;
-    }
-    if constexpr (MODE == MODE_MX) s_e[buf][t] = re;
   };
 
-  // Fragment reads: two 16-byte chunks of row r at (chunk ^ (r & 7)); r & 7 == lane & 7.
+  // Fragment reads: two 16-byte chunks of row r (r & 15 == lane & 15).
   // Exact path: chunks 2g, 2g+1 (K 32g..32g+31); fast path: chunks g, 4+g.
-  const int g = lane >> 4, xr = lane & 7;
-  const int c0 = (PATH == PATH_EXACT ? 2 * g : g) ^ xr;
-  const int c1 = (PATH == PATH_EXACT ? 2 * g + 1 : 4 + g) ^ xr;
-  int fa_off[4], fb_off[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    fa_off[i] = (wm * 64 + i * 16 + (lane & 15)) * 128;
-    fb_off[i] = TBM * TBK + (wn * 64 + i * 16 + (lane & 15)) * 128;
-  }
+  const int g = lane >> 4, sw_ = lds_swz(lane & 15);
+  const int c0 = ((PATH == PATH_EXACT ? 2 * g : g) ^ sw_) << 4;
+  const int c1 = ((PATH == PATH_EXACT ? 2 * g + 1 : 4 + g) ^ sw_) << 4;
+  const int a_row0 = wm * 128 + (lane & 15);       // + 16 i
+  const int b_row0 = wn * 64 + (lane & 15);        // + 16 j
+  // column block of this wave's 64 columns (for 128x128 weight blocks); a wave
+  // whose columns all lie past N (ragged last tile) reads the last block
+  const int64_t nblk_raw = (n0 + wn * 64) / 128, nblk_max = (N + 127) / 128 - 1;
+  const int64_t nblk = nblk_raw < nblk_max ? nblk_raw : nblk_max;
 
-  v4f acc[4][4];
+  v4f acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (nkb > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
+  if (nkb > 0) issue_loads(0, 0);
 
   for (int kb = 0; kb < nkb; ++kb) {
     const int buf = kb & 1;
-    if (kb + 1 < nkb) gload(kb + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kb + 1 < nkb) issue_loads(kb + 1, buf ^ 1);
 
-    auto lds16 = [&](int off) { return *reinterpret_cast<const u32x4*>(&smem[buf][off]); };
-    u32x4 lb[4][2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lb[j][0] = lds16(fb_off[j] + (c0 << 4));
-      lb[j][1] = lds16(fb_off[j] + (c1 << 4));
-    }
+    const uint8_t* sa_ = &smem[buf][0];
+    const uint8_t* sb_ = &smem[buf][TBM * TBK];
+    auto lds16 = [&](const uint8_t* base, int off) { return *reinterpret_cast<const u32x4*>(base + off); };
 
-    // promotion scale of this step for A tile i: sA[row, kb] * sB[n0/128, kb] for the lane's 4 rows
     float swv = 1.0f;
-    if constexpr (MODE == MODE_PROMOTE) swv = swb[(n0 / 128) * nkb + kb];
-    auto promo_scale = [&](int i) {
-      const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * 64 + i * 16 + 4 * g]);
-      return v4f{sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};
-    };
-    // MX: this lane's scale byte (block g of the step) for each A and B tile
-    uint32_t ea[4] = {0, 0, 0, 0}, eb[4] = {0, 0, 0, 0};
-    if constexpr (MODE == MODE_MX) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ea[i] = (s_e[buf][wm * 64 + i * 16 + (lane & 15)] >> (8 * g)) & 0xffu;
-        eb[i] = (s_e[buf][TBM + wn * 64 + i * 16 + (lane & 15)] >> (8 * g)) & 0xffu;
-      }
-    }
+    if constexpr (MODE == MODE_PROMOTE) swv = swb[nblk * nkb + kb];
 
     if constexpr (PATH == PATH_FAST) {
-      v8i fa[4], fb[4];
+      v8i fb[4];
+      int eb[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa[i] = join(lds16(fa_off[i] + (c0 << 4)), lds16(fa_off[i] + (c1 << 4)));
-        fb[i] = join(lb[i][0], lb[i][1]);
+      for (int j = 0; j < 4; ++j) {
+        const int r = b_row0 + 16 * j;
+        fb[j] = join(lds16(sb_, r * 128 + c0), lds16(sb_, r * 128 + c1));
+        if constexpr (MODE == MODE_MX) eb[j] = (int)((s_e[buf][TBM + r] >> (8 * g)) & 0xffu);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i) {
+        const int r = a_row0 + 16 * i;
+        const v8i fa = join(lds16(sa_, r * 128 + c0), lds16(sa_, r * 128 + c1));
+        if constexpr (MODE == MODE_PROMOTE) {
+          const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * 128 + 16 * i + 4 * g]);
+          const v4f sc = {sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (MODE == MODE_EPILOGUE) {
-            acc[i][j] = mfma_fp8<AF, BF>(fa[i], fb[j], acc[i][j], (int)kUnitScale, (int)kUnitScale);
-          } else if constexpr (MODE == MODE_PROMOTE) {
-            const v4f pr = mfma_fp8<AF, BF>(fa[i], fb[j], v4f{0.0f, 0.0f, 0.0f, 0.0f}, (int)kUnitScale,
-                                            (int)kUnitScale);
-            const v4f sc = promo_scale(i);
+          for (int j = 0; j < 4; ++j) {
+            const v4f pr = mfma_fp8<AF, BF>(fa, fb[j], v4f{0.0f, 0.0f, 0.0f, 0.0f}, (int)kUnitScale, (int)kUnitScale);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pr[r], sc[r], acc[i][j][r]);
-          } else {
-            acc[i][j] = mfma_fp8<AF, BF>(fa[i], fb[j], acc[i][j], (int)ea[i], (int)eb[j]);
+            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(pr[q], sc[q], acc[i][j][q]);
           }
+        } else if constexpr (MODE == MODE_MX) {
+          const int ea = (int)((s_e[buf][r] >> (8 * g)) & 0xffu);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp8<AF, BF>(fa, fb[j], acc[i][j], ea, eb[j]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = mfma_fp8<AF, BF>(fa, fb[j], acc[i][j], (int)kUnitScale, (int)kUnitScale);
         }
+      }
     } else {
-      // Exact path: four K=32 sub-steps; operands expanded to bf16 with the MX
-      // scale (or 1) folded in.  B tiles are converted once per step; A tiles
-      // one at a time, each feeding four independent accumulation chains.
+      // Exact path: four K=32 sub-steps on bf16 operands (MX scales folded in).
       v8bf xb[4][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float fsb = (MODE == MODE_MX) ? e8m0_to_f32(eb[j]) : 1.0f;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4 d = lb[j][s >> 1];
-          xb[j][s] = (s & 1) ? cvt8<BF>(d.z, d.w, fsb) : cvt8<BF>(d.x, d.y, fsb);
-        }
+        const int r = b_row0 + 16 * j;
+        const float fsb = (MODE == MODE_MX) ? e8m0_to_f32((s_e[buf][TBM + r] >> (8 * g)) & 0xffu) : 1.0f;
+        const u32x4 d0 = lds16(sb_, r * 128 + c0), d1 = lds16(sb_, r * 128 + c1);
+        xb[j][0] = cvt8<BF>(d0.x, d0.y, fsb);
+        xb[j][1] = cvt8<BF>(d0.z, d0.w, fsb);
+        xb[j][2] = cvt8<BF>(d1.x, d1.y, fsb);
+        xb[j][3] = cvt8<BF>(d1.z, d1.w, fsb);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float fsa = (MODE == MODE_MX) ? e8m0_to_f32(ea[i]) : 1.0f;
-        const u32x4 la0 = lds16(fa_off[i] + (c0 << 4)), la1 = lds16(fa_off[i] + (c1 << 4));
+      if constexpr (MODE == MODE_PROMOTE) {
+        // Software-pipelined order: A tile i+1 is read and converted while
+        // tile i multiplies; each N tile is a chain of four dependent MFMAs
+        // (the 128-K partial P), and chain j-1 is promoted into the fp32
+        // accumulator while chain j runs.
+        u32x4 n0 = lds16(sa_, a_row0 * 128 + c0), n1 = lds16(sa_, a_row0 * 128 + c1);
         v8bf xa[4];
+        xa[0] = cvt8<AF>(n0.x, n0.y, 1.0f);
+        xa[1] = cvt8<AF>(n0.z, n0.w, 1.0f);
+        xa[2] = cvt8<AF>(n1.x, n1.y, 1.0f);
+        xa[3] = cvt8<AF>(n1.z, n1.w, 1.0f);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4 d = (s >> 1) ? la1 : la0;
-          xa[s] = (s & 1) ? cvt8<AF>(d.z, d.w, fsa) : cvt8<AF>(d.x, d.y, fsa);
+        for (int i = 0; i < 8; ++i) {
+          if (i + 1 < 8) {
+            const int r = a_row0 + 16 * (i + 1);
+            n0 = lds16(sa_, r * 128 + c0);
+            n1 = lds16(sa_, r * 128 + c1);
+          }
+          const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * 128 + 16 * i + 4 * g]);
+          const v4f sc = {sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};
+          v4f prev = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v4f pp = mfma_bf16(xa[0], xb[j][0], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+            pp = mfma_bf16(xa[1], xb[j][1], pp);
+            pp = mfma_bf16(xa[2], xb[j][2], pp);
+            pp = mfma_bf16(xa[3], xb[j][3], pp);
+            if (j > 0) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[i][j - 1][q] = __builtin_fmaf(prev[q], sc[q], acc[i][j - 1][q]);
+            }
+            prev = pp;
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[i][3][q] = __builtin_fmaf(prev[q], sc[q], acc[i][3][q]);
+          if (i + 1 < 8) {
+            xa[0] = cvt8<AF>(n0.x, n0.y, 1.0f);
+            xa[1] = cvt8<AF>(n0.z, n0.w, 1.0f);
+            xa[2] = cvt8<AF>(n1.x, n1.y, 1.0f);
+            xa[3] = cvt8<AF>(n1.z, n1.w, 1.0f);
+          }
         }
-        if constexpr (MODE == MODE_PROMOTE) {
-          v4f pp[4];
+      } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) pp[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pp[j] = mfma_bf16(xa[s], xb[j][s], pp[j]);
-          const v4f sc = promo_scale(i);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(pp[j][r], sc[r], acc[i][j][r]);
-        } else {
+        for (int i = 0; i < 8; ++i) {
+          const int r = a_row0 + 16 * i;
+          const float fsa = (MODE == MODE_MX) ? e8m0_to_f32((s_e[buf][r] >> (8 * g)) & 0xffu) : 1.0f;
+          const u32x4 d0 = lds16(sa_, r * 128 + c0), d1 = lds16(sa_, r * 128 + c1);
+          v8bf xa[4];
+          xa[0] = cvt8<AF>(d0.x, d0.y, fsa);
+          xa[1] = cvt8<AF>(d0.z, d0.w, fsa);
+          xa[2] = cvt8<AF>(d1.x, d1.y, fsa);
+          xa[3] = cvt8<AF>(d1.z, d1.w, fsa);
 #pragma unroll
           for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -325,15 +371,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs p) {
         }
       }
     }
-
-    if (kb + 1 < nkb) lstore(buf ^ 1);
-    __syncthreads();
   }
 
   // epilogue
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t rbase = m0 + wm * 64 + i * 16;
+  for (int i = 0; i < 8; ++i) {
+    const int64_t rbase = m0 + wm * 128 + i * 16;
     if (rbase >= M) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -343,14 +386,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tiled(GemmArgs p) {
       float sbv = 1.0f;
       if constexpr (MODE == MODE_EPILOGUE) sbv = swb[p.b_per_row ? col : 0];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = rbase + 4 * g + r;
-        float v = acc[i][j][r];
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = rbase + 4 * g + q;
+        float v = acc[i][j][q];
         if constexpr (MODE == MODE_EPILOGUE) v = v * (sxa[p.a_per_row ? row : 0] * sbv);
         store_out<ODT>(p.out, row * N + col, v);
       }
     }
   }
+}
+
+// Kernels for the two workgroup shapes (256x256 with 8 waves, 128x256 with 4).
+template <int AF, int BF, int MODE, int ODT, int PATH>
+__global__ __launch_bounds__(512, 1) void k_gemm_tiled_256x256(GemmArgs p) {
+  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4>(p);
+}
+template <int AF, int BF, int MODE, int ODT, int PATH>
+__global__ __launch_bounds__(256, 1) void k_gemm_tiled_128x256(GemmArgs p) {
+  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 1, 4>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -504,33 +557,56 @@ hipError_t launch_fill_zero(void* out, int64_t bytes, hipStream_t st) {
   return hipGetLastError();
 }
 
-// ---- dispatch over formats, modes, output dtype and path ----------------------
+// ---- dispatch over formats, modes, output dtype, path and tile shape ---------
+// Tile shapes: 256x256 (8 waves) when that gives at least one tile per CU,
+// else 128x256 (4 waves).
+static int num_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+template <int AF, int BF, int MODE, int ODT, int PATH>
+static void tiled_shape(const GemmArgs& p, hipStream_t st) {
+  const int64_t big_tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+  if (big_tiles >= num_cus()) {
+    hipLaunchKernelGGL((k_gemm_tiled_256x256<AF, BF, MODE, ODT, PATH>), dim3((unsigned)big_tiles), dim3(512), 0, st, p);
+  } else {
+    const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 255) / 256);
+    hipLaunchKernelGGL((k_gemm_tiled_128x256<AF, BF, MODE, ODT, PATH>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+  }
+}
+
 template <int AF, int BF, int MODE, int ODT>
-static void tiled_path(const GemmArgs& p, int path, dim3 grid, hipStream_t st) {
-  if (path == PATH_FAST) hipLaunchKernelGGL((k_gemm_tiled<AF, BF, MODE, ODT, PATH_FAST>), grid, dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((k_gemm_tiled<AF, BF, MODE, ODT, PATH_EXACT>), grid, dim3(256), 0, st, p);
+static void tiled_path(const GemmArgs& p, int path, hipStream_t st) {
+  if (path == PATH_FAST) tiled_shape<AF, BF, MODE, ODT, PATH_FAST>(p, st);
+  else tiled_shape<AF, BF, MODE, ODT, PATH_EXACT>(p, st);
 }
 
 template <int AF, int BF, int MODE>
-static void tiled_odt(const GemmArgs& p, int odt, int path, dim3 grid, hipStream_t st) {
-  if (odt == DT_F32) tiled_path<AF, BF, MODE, DT_F32>(p, path, grid, st);
-  else tiled_path<AF, BF, MODE, DT_BF16>(p, path, grid, st);
+static void tiled_odt(const GemmArgs& p, int odt, int path, hipStream_t st) {
+  if (odt == DT_F32) tiled_path<AF, BF, MODE, DT_F32>(p, path, st);
+  else tiled_path<AF, BF, MODE, DT_BF16>(p, path, st);
 }
 
 template <int AF, int BF>
-static void tiled_mode(const GemmArgs& p, int mode, int odt, int path, dim3 grid, hipStream_t st) {
-  if (mode == MODE_EPILOGUE) tiled_odt<AF, BF, MODE_EPILOGUE>(p, odt, path, grid, st);
-  else if (mode == MODE_PROMOTE) tiled_odt<AF, BF, MODE_PROMOTE>(p, odt, path, grid, st);
-  else tiled_odt<AF, BF, MODE_MX>(p, odt, path, grid, st);
+static void tiled_mode(const GemmArgs& p, int mode, int odt, int path, hipStream_t st) {
+  if (mode == MODE_EPILOGUE) tiled_odt<AF, BF, MODE_EPILOGUE>(p, odt, path, st);
+  else if (mode == MODE_PROMOTE) tiled_odt<AF, BF, MODE_PROMOTE>(p, odt, path, st);
+  else tiled_odt<AF, BF, MODE_MX>(p, odt, path, st);
 }
 
 hipError_t launch_gemm_tiled(const GemmArgs& p, int afmt, int bfmt, int mode, int odt, int path, hipStream_t st) {
-  const int64_t ntm = (p.M + TBM - 1) / TBM, ntn = (p.N + TBN - 1) / TBN;
-  const dim3 grid((unsigned)(ntm * ntn));
-  if (afmt == FMT_E4M3 && bfmt == FMT_E4M3) tiled_mode<FMT_E4M3, FMT_E4M3>(p, mode, odt, path, grid, st);
-  else if (afmt == FMT_E4M3) tiled_mode<FMT_E4M3, FMT_E5M2>(p, mode, odt, path, grid, st);
-  else if (bfmt == FMT_E4M3) tiled_mode<FMT_E5M2, FMT_E4M3>(p, mode, odt, path, grid, st);
-  else tiled_mode<FMT_E5M2, FMT_E5M2>(p, mode, odt, path, grid, st);
+  if (afmt == FMT_E4M3 && bfmt == FMT_E4M3) tiled_mode<FMT_E4M3, FMT_E4M3>(p, mode, odt, path, st);
+  else if (afmt == FMT_E4M3) tiled_mode<FMT_E4M3, FMT_E5M2>(p, mode, odt, path, st);
+  else if (bfmt == FMT_E4M3) tiled_mode<FMT_E5M2, FMT_E4M3>(p, mode, odt, path, st);
+  else tiled_mode<FMT_E5M2, FMT_E5M2>(p, mode, odt, path, st);
   return hipGetLastError();
 }
 
