@@ -11,6 +11,10 @@ using namespace fp8blk;
 
 namespace {
 
+// Largest GEMM K: the kernels address up to 256 operand rows (256 * K bytes)
+// plus an out-of-range sentinel through 32-bit buffer offsets.
+constexpr int64_t kMaxGemmK = int64_t(1) << 22;
+
 bool valid_fmt(fp8_format_t f) { return f == FP8_E4M3 || f == FP8_E5M2; }
 bool valid_dt(fp8_dtype_t d) { return d == FP8_DT_F32 || d == FP8_DT_BF16; }
 bool valid_gran(fp8_granularity_t g) { return g >= FP8_GRAN_TENSOR && g <= FP8_GRAN_MX32; }
@@ -45,7 +49,7 @@ const char* fp8_status_string(fp8_status_t st) {
     case FP8_OK: return "ok";
     case FP8_ERR_NULL: return "a required pointer is NULL";
     case FP8_ERR_ENUM: return "invalid format, granularity, dtype or algorithm value";
-    case FP8_ERR_SHAPE: return "invalid shape (negative, K % 128, rows % 128 for 128x128 blocks, M/N % 16, or too large)";
+    case FP8_ERR_SHAPE: return "invalid shape (negative, K % 128, rows % 128 for 128x128 blocks, M/N % 16, GEMM K > 2^22, or too large)";
     case FP8_ERR_UNSUPPORTED: return "unsupported combination";
     case FP8_ERR_WORKSPACE: return "workspace missing or too small";
     case FP8_ERR_HIP: return "HIP launch failed";
@@ -112,6 +116,7 @@ fp8_status_t fp8_gemm_blockscaled_ex(const uint8_t* a, fp8_format_t a_fmt, fp8_g
   if (algo != FP8_GEMM_AUTO && algo != FP8_GEMM_TILED && algo != FP8_GEMM_SKINNY) return FP8_ERR_ENUM;
   if (accum != FP8_ACCUM_FP32 && accum != FP8_ACCUM_NATIVE) return FP8_ERR_ENUM;
   if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 128) return FP8_ERR_SHAPE;
+  if (K > kMaxGemmK) return FP8_ERR_SHAPE;
   if (mul_checked(M, K) < 0 || mul_checked(N, K) < 0 || mul_checked(M, N) < 0) return FP8_ERR_SHAPE;
   if ((M / 128 + 1) * (N / 128 + 1) >= INT_MAX || N / 16 >= INT_MAX) return FP8_ERR_SHAPE;
 

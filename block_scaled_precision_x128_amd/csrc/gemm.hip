@@ -39,73 +39,9 @@
 //   MODE_MX        32-element UE8M0 blocks: 2^(eA+eB) applied per 32-K block,
 //                  folded into the bf16 operands (exact path) or given to the
 //                  scaled MFMA (fast path)
-#include "device_common.h"
-#include "kernels.h"
+#include "gemm_common.h"
 
 namespace fp8blk {
-
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-
-constexpr uint32_t kUnitScale = 0x7f7f7f7fu;  // E8M0 127 = 2^0 in every byte
-// Word 3 of a gfx9 buffer descriptor for raw byte-addressed access.
-constexpr int kBufferFlags = 0x00020000;
-
-// 16-byte load through a buffer descriptor; offsets at or past the
-// descriptor's size read as zero.
-__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, int voff) {
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
-  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
-  return u32x4{(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
-}
-
-template <int AF, int BF>
-__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, sa, 0, sb);
-}
-
-__device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ v8i join(const u32x4& lo, const u32x4& hi) {
-  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
-// 2 FP8 codes (16-bit word `hi` of w) -> 2 bf16, multiplied by `scale` (a power of two or 1).
-template <int FMT>
-__device__ __forceinline__ v2bf cvt2(uint32_t w, float scale, bool hi) {
-  if constexpr (FMT == FMT_E4M3) {
-    return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, true)
-              : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, false);
-  } else {
-    return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, scale, true)
-              : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, scale, false);
-  }
-}
-
-// The 8 codes of dwords (d0, d1) -> one K=32 bf16 operand.
-template <int FMT>
-__device__ __forceinline__ v8bf cvt8(uint32_t d0, uint32_t d1, float scale) {
-  const v2bf p0 = cvt2<FMT>(d0, scale, false), p1 = cvt2<FMT>(d0, scale, true);
-  const v2bf p2 = cvt2<FMT>(d1, scale, false), p3 = cvt2<FMT>(d1, scale, true);
-  return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-// 2^(byte - 127) as fp32 (byte 0 gives the subnormal 2^-127).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t byte) {
-  return byte ? __uint_as_float(byte << 23) : __uint_as_float(0x00400000u);
-}
-
-template <int ODT>
-__device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
-  if constexpr (ODT == DT_F32) {
-    reinterpret_cast<float*>(out)[idx] = v;
-  } else {
-    const __bf16 h = (__bf16)v;
-    reinterpret_cast<uint16_t*>(out)[idx] = __builtin_bit_cast(uint16_t, h);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Tiled kernel: 256x256 output tile per workgroup of 8 waves (2 along M x 4
@@ -407,143 +343,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_tiled_128x256(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Skinny kernel for decode shapes (M <= 64): W is streamed once from HBM
-// straight into matrix-core registers.  One workgroup per 16 output columns;
-// the 4 waves take contiguous quarters of K and add their partial tiles in
-// LDS at the end.
-// ---------------------------------------------------------------------------
-template <int AF, int BF, int MODE, int ODT, int PATH, int MT>
-__global__ __launch_bounds__(256) void k_gemm_skinny(GemmArgs p) {
-  constexpr int U = 4;  // 128-K steps loaded ahead per wave
-  __shared__ __attribute__((aligned(16))) float red[4][MT][64][4];
-  const int64_t M = p.M, N = p.N, K = p.K;
-  const int nkb = (int)(K / 128);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t nrow = n0 + (lane & 15);
-  const int kb0 = (int)((int64_t)w * nkb / 4), kb1 = (int)((int64_t)(w + 1) * nkb / 4);
-  // byte offsets of this lane's two 16-byte pieces inside a 128-K step
-  const int o0 = PATH == PATH_EXACT ? 32 * g : 16 * g;
-  const int o1 = PATH == PATH_EXACT ? 32 * g + 16 : 64 + 16 * g;
-
-  const uint8_t* bp = p.b + nrow * K;
-  const uint8_t* ap[MT];
-  int64_t arow[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int64_t r = mt * 16 + (lane & 15);
-    arow[mt] = r < M ? r : M - 1;
-    ap[mt] = p.a + arow[mt] * K;
-  }
-  const float* sxa = reinterpret_cast<const float*>(p.sa);
-  const float* swb = reinterpret_cast<const float*>(p.sb);
-  const uint8_t* eab = reinterpret_cast<const uint8_t*>(p.sa);
-  const uint8_t* ebb = reinterpret_cast<const uint8_t*>(p.sb);
-  const int64_t kq = K / 32;
-
-  v4f acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  u32x4 bq[U][2];
-  u32x4 aq[U][MT][2];
-  for (int kb = kb0; kb < kb1; kb += U) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (kb + u < kb1) {
-        const int64_t kk = (int64_t)(kb + u) * 128;
-        bq[u][0] = *reinterpret_cast<const u32x4*>(bp + kk + o0);
-        bq[u][1] = *reinterpret_cast<const u32x4*>(bp + kk + o1);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          aq[u][mt][0] = *reinterpret_cast<const u32x4*>(ap[mt] + kk + o0);
-          aq[u][mt][1] = *reinterpret_cast<const u32x4*>(ap[mt] + kk + o1);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = kb + u;
-      if (k >= kb1) continue;
-      float swv = 1.0f;
-      if constexpr (MODE == MODE_PROMOTE) swv = swb[(n0 / 128) * nkb + k];
-      const uint32_t eb = (MODE == MODE_MX) ? (uint32_t)ebb[nrow * kq + k * 4 + g] : 127u;
-      if constexpr (PATH == PATH_FAST) {
-        const v8i fb = join(bq[u][0], bq[u][1]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const v8i fa = join(aq[u][mt][0], aq[u][mt][1]);
-          if constexpr (MODE == MODE_PROMOTE) {
-            const v4f pr = mfma_fp8<AF, BF>(fa, fb, v4f{0.0f, 0.0f, 0.0f, 0.0f}, (int)kUnitScale, (int)kUnitScale);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              int64_t row = mt * 16 + 4 * g + r;
-              row = row < M ? row : M - 1;
-              acc[mt][r] = __builtin_fmaf(pr[r], sxa[row * nkb + k] * swv, acc[mt][r]);
-            }
-          } else if constexpr (MODE == MODE_MX) {
-            const int ea = (int)eab[arow[mt] * kq + k * 4 + g];
-            acc[mt] = mfma_fp8<AF, BF>(fa, fb, acc[mt], ea, (int)eb);
-          } else {
-            acc[mt] = mfma_fp8<AF, BF>(fa, fb, acc[mt], (int)kUnitScale, (int)kUnitScale);
-          }
-        }
-      } else {
-        const float fsb = (MODE == MODE_MX) ? e8m0_to_f32(eb) : 1.0f;
-        v8bf xb[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4 d = bq[u][s >> 1];
-          xb[s] = (s & 1) ? cvt8<BF>(d.z, d.w, fsb) : cvt8<BF>(d.x, d.y, fsb);
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const float fsa = (MODE == MODE_MX) ? e8m0_to_f32((uint32_t)eab[arow[mt] * kq + k * 4 + g]) : 1.0f;
-          v8bf xa[4];
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const u32x4 d = aq[u][mt][s >> 1];
-            xa[s] = (s & 1) ? cvt8<AF>(d.z, d.w, fsa) : cvt8<AF>(d.x, d.y, fsa);
-          }
-          if constexpr (MODE == MODE_PROMOTE) {
-            v4f pp = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) pp = mfma_bf16(xa[s], xb[s], pp);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              int64_t row = mt * 16 + 4 * g + r;
-              row = row < M ? row : M - 1;
-              acc[mt][r] = __builtin_fmaf(pp[r], sxa[row * nkb + k] * swv, acc[mt][r]);
-            }
-          } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) acc[mt] = mfma_bf16(xa[s], xb[s], acc[mt]);
-          }
-        }
-      }
-    }
-  }
-
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    *reinterpret_cast<float4*>(&red[w][mt][lane][0]) = make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
-  __syncthreads();
-  // wave w finishes M-tiles mt = w, w+4, ...
-  for (int mt = w; mt < MT; mt += 4) {
-    const int64_t rbase = mt * 16;
-    if (rbase >= M) continue;
-    const int64_t col = nrow;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v = red[0][mt][lane][r] + red[1][mt][lane][r] + red[2][mt][lane][r] + red[3][mt][lane][r];
-      const int64_t row = rbase + 4 * g + r;
-      if constexpr (MODE == MODE_EPILOGUE) v = v * (sxa[p.a_per_row ? row : 0] * swb[p.b_per_row ? col : 0]);
-      store_out<ODT>(p.out, row * N + col, v);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 __global__ void k_fill_zero(uint32_t* p, int64_t nwords) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < nwords) p[i] = 0u;
@@ -560,17 +359,6 @@ hipError_t launch_fill_zero(void* out, int64_t bytes, hipStream_t st) {
 // ---- dispatch over formats, modes, output dtype, path and tile shape ---------
 // Tile shapes: 256x256 (8 waves) when that gives at least one tile per CU,
 // else 128x256 (4 waves).
-static int num_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-    else
-      cus = 256;
-  }
-  return cus;
-}
 
 template <int AF, int BF, int MODE, int ODT, int PATH>
 static void tiled_shape(const GemmArgs& p, hipStream_t st) {
@@ -607,42 +395,6 @@ hipError_t launch_gemm_tiled(const GemmArgs& p, int afmt, int bfmt, int mode, in
   else if (afmt == FMT_E4M3) tiled_mode<FMT_E4M3, FMT_E5M2>(p, mode, odt, path, st);
   else if (bfmt == FMT_E4M3) tiled_mode<FMT_E5M2, FMT_E4M3>(p, mode, odt, path, st);
   else tiled_mode<FMT_E5M2, FMT_E5M2>(p, mode, odt, path, st);
-  return hipGetLastError();
-}
-
-template <int AF, int BF, int MODE, int ODT, int PATH>
-static void skinny_mt(const GemmArgs& p, dim3 grid, hipStream_t st) {
-  const int64_t mt = (p.M + 15) / 16;
-  if (mt <= 1) hipLaunchKernelGGL((k_gemm_skinny<AF, BF, MODE, ODT, PATH, 1>), grid, dim3(256), 0, st, p);
-  else if (mt <= 2) hipLaunchKernelGGL((k_gemm_skinny<AF, BF, MODE, ODT, PATH, 2>), grid, dim3(256), 0, st, p);
-  else hipLaunchKernelGGL((k_gemm_skinny<AF, BF, MODE, ODT, PATH, 4>), grid, dim3(256), 0, st, p);
-}
-
-template <int AF, int BF, int MODE, int ODT>
-static void skinny_path(const GemmArgs& p, int path, dim3 grid, hipStream_t st) {
-  if (path == PATH_FAST) skinny_mt<AF, BF, MODE, ODT, PATH_FAST>(p, grid, st);
-  else skinny_mt<AF, BF, MODE, ODT, PATH_EXACT>(p, grid, st);
-}
-
-template <int AF, int BF, int MODE>
-static void skinny_odt(const GemmArgs& p, int odt, int path, dim3 grid, hipStream_t st) {
-  if (odt == DT_F32) skinny_path<AF, BF, MODE, DT_F32>(p, path, grid, st);
-  else skinny_path<AF, BF, MODE, DT_BF16>(p, path, grid, st);
-}
-
-template <int AF, int BF>
-static void skinny_mode(const GemmArgs& p, int mode, int odt, int path, dim3 grid, hipStream_t st) {
-  if (mode == MODE_EPILOGUE) skinny_odt<AF, BF, MODE_EPILOGUE>(p, odt, path, grid, st);
-  else if (mode == MODE_PROMOTE) skinny_odt<AF, BF, MODE_PROMOTE>(p, odt, path, grid, st);
-  else skinny_odt<AF, BF, MODE_MX>(p, odt, path, grid, st);
-}
-
-hipError_t launch_gemm_skinny(const GemmArgs& p, int afmt, int bfmt, int mode, int odt, int path, hipStream_t st) {
-  const dim3 grid((unsigned)(p.N / 16));
-  if (afmt == FMT_E4M3 && bfmt == FMT_E4M3) skinny_mode<FMT_E4M3, FMT_E4M3>(p, mode, odt, path, grid, st);
-  else if (afmt == FMT_E4M3) skinny_mode<FMT_E4M3, FMT_E5M2>(p, mode, odt, path, grid, st);
-  else if (bfmt == FMT_E4M3) skinny_mode<FMT_E5M2, FMT_E4M3>(p, mode, odt, path, grid, st);
-  else skinny_mode<FMT_E5M2, FMT_E5M2>(p, mode, odt, path, grid, st);
   return hipGetLastError();
 }
 

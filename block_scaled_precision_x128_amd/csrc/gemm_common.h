@@ -1,0 +1,91 @@
+// Device helpers shared by the GEMM kernels (gemm.hip, gemm_skinny.hip):
+// matrix-core wrappers, FP8 -> bf16 operand expansion, buffer-descriptor
+// loads and output stores.  See gemm.hip for the operand layouts.
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace fp8blk {
+
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kUnitScale = 0x7f7f7f7fu;  // E8M0 127 = 2^0 in every byte
+// Word 3 of a gfx9 buffer descriptor for raw byte-addressed access.
+constexpr int kBufferFlags = 0x00020000;
+
+// 16-byte load through a buffer descriptor; offsets at or past the
+// descriptor's size read as zero.
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, int voff) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
+  return u32x4{(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+}
+
+template <int AF, int BF>
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v8i join(const u32x4& lo, const u32x4& hi) {
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// 2 FP8 codes (16-bit word `hi` of w) -> 2 bf16, multiplied by `scale` (a power of two or 1).
+template <int FMT>
+__device__ __forceinline__ v2bf cvt2(uint32_t w, float scale, bool hi) {
+  if constexpr (FMT == FMT_E4M3) {
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, false);
+  } else {
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, scale, true)
+              : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, scale, false);
+  }
+}
+
+// The 8 codes of dwords (d0, d1) -> one K=32 bf16 operand.
+template <int FMT>
+__device__ __forceinline__ v8bf cvt8(uint32_t d0, uint32_t d1, float scale) {
+  const v2bf p0 = cvt2<FMT>(d0, scale, false), p1 = cvt2<FMT>(d0, scale, true);
+  const v2bf p2 = cvt2<FMT>(d1, scale, false), p3 = cvt2<FMT>(d1, scale, true);
+  return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// 2^(byte - 127) as fp32 (byte 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t byte) {
+  return byte ? __uint_as_float(byte << 23) : __uint_as_float(0x00400000u);
+}
+
+template <int ODT>
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
+  if constexpr (ODT == DT_F32) {
+    reinterpret_cast<float*>(out)[idx] = v;
+  } else {
+    const __bf16 h = (__bf16)v;
+    reinterpret_cast<uint16_t*>(out)[idx] = __builtin_bit_cast(uint16_t, h);
+  }
+}
+
+// Buffer offset that lies past every descriptor's range: loads through it
+// return zeros without touching memory.
+constexpr int kOutOfRange = 0x7ff00000;
+
+// Compute units of the current device (cached per device).
+inline int num_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    cus[dev] = (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ? v : 256;
+  }
+  return cus[dev];
+}
+
+}  // namespace fp8blk

@@ -106,7 +106,8 @@ typedef enum {
   FP8_ERR_NULL = 1,        /* a required pointer is NULL                          */
   FP8_ERR_ENUM = 2,        /* a format / granularity / dtype / algo value is invalid */
   FP8_ERR_SHAPE = 3,       /* negative size, K % 128 != 0, rows % 128 != 0 for     */
-                           /* 128x128 blocks, M or N % 16 != 0 for the GEMM         */
+                           /* 128x128 blocks, M or N % 16 != 0 or K > 2^22 for the  */
+                           /* GEMM                                                  */
   FP8_ERR_UNSUPPORTED = 4, /* a valid but unsupported combination                 */
   FP8_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required          */
   FP8_ERR_HIP = 6,         /* a HIP launch failed                                  */
@@ -177,8 +178,9 @@ fp8_status_t fp8_cast(const void* x, fp8_dtype_t x_dt, int64_t n, fp8_format_t f
  *   MX32 x MX32                power-of-two scales applied per 32-K block by
  *                              the scaled matrix-core instruction
  * Any other pair returns FP8_ERR_UNSUPPORTED.  Formats may differ per operand.
- * Shapes: M % 16 == 0, N % 16 == 0, K % 128 == 0; N % 128 == 0 for a
- * BLOCK_128x128 b.  K == 0 writes zeros. */
+ * Shapes: M % 16 == 0, N % 16 == 0, K % 128 == 0, K <= 2^22 (the kernels
+ * address up to 256 operand rows through 32-bit buffer offsets); N % 128 == 0
+ * for a BLOCK_128x128 b.  K == 0 writes zeros. */
 fp8_status_t fp8_gemm_blockscaled(const uint8_t* a, fp8_format_t a_fmt, fp8_granularity_t a_g,
                                   const void* a_scales,
                                   const uint8_t* b, fp8_format_t b_fmt, fp8_granularity_t b_g,

@@ -101,6 +101,7 @@ def test_gemm_validation(lib):
     assert g(*args(BL, BL)) == 4
     assert g(*args(T, T, M=24)) == 3         # M % 16
     assert g(*args(T, T, K=200)) == 3        # K % 128
+    assert g(*args(T, T, K=(1 << 22) + 128)) == 3   # K beyond 32-bit buffer offsets
     assert g(*args(TL, BL, N=144)) == 3      # 128x128 blocks need N % 128
     assert g(*args(T, T, algo=5)) == 2
     assert g(*args(T, T, M=128, algo=fb.GEMM_SKINNY)) == 4
