@@ -16,7 +16,18 @@ Input sets are rotated (R copies, over 1 GB in total) so that no launch
 reads data another launch left in the 256 MB last-level cache.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--copy-probe]
+                    [--accum fp32|native] [--no-cpu-baseline] [--copy-probe]
+
+For the decode workload (c4_decode_skinny) W is quantized once per input set
+in setup, as a model's weights are, and a step is quantize X + GEMM.
+
+Profiling helpers (no GPU needed; they read rocprofv3 output):
+    python bench.py --summarize-trace DIR       kernel-trace --stats summary
+    python bench.py --summarize-traffic ...     HBM bytes of the GEMM from two
+                                                --pmc runs, calibrated by a copy
+`roofline.traffic` is filled from profiles/traffic_<workload>_<accum>.txt when
+that file was taken from the GEMM sources as they are now (a SHA-256 of them
+is stored in it), and is null otherwise.
 """
 
 from __future__ import annotations
@@ -38,6 +49,7 @@ METRIC = "block-scaled FP8 GEMM TFLOP/s (% fp8 MFMA peak); quantize GB/s (% HBM)
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 matrix-core peak
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak
+COPY_PROBE_BYTES = 256 << 20  # size of the plain copy that calibrates the byte counters
 
 
 def scale_bytes(gran: int, rows: int, cols: int) -> int:
@@ -87,6 +99,105 @@ def cpu_baseline(wl, sample_rows: int):
                       f"plus fp64 GEMM and bound; {dt:.2f} s; numpy BLAS threads={threads}, quantize 1 thread"}
 
 
+GEMM_SOURCES = ("gemm.hip", "gemm_skinny.hip", "gemm_common.h", "device_common.h", "kernels.h")
+
+
+def gemm_source_hash() -> str:
+    """SHA-256 over the GEMM kernel sources (counter summaries are valid only for these)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "block_scaled_precision_x128_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload: str, accum: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}_{accum}.txt")
+
+
+def read_traffic(workload: str, accum: str):
+    """HBM bytes per GEMM launch from a stored counter summary, or None when
+    there is none or it was taken from other kernel sources."""
+    path = traffic_path(workload, accum)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != gemm_source_hash() or "traffic_bytes_per_launch" not in kv:
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
+
+
+def _sqlite_db(d: str) -> str:
+    import glob
+    dbs = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 database under {d}")
+    return dbs[0]
+
+
+def summarize_trace(d: str) -> str:
+    """Per-kernel call count and mean/total duration from a rocprofv3
+    --kernel-trace --stats database."""
+    import sqlite3
+    con = sqlite3.connect(_sqlite_db(d))
+    rows = list(con.execute("select name, total_calls, total_duration, average, percentage from top_kernels"))
+    out = [f"{'calls':>6} {'mean_us':>10} {'total_us':>11} {'pct':>6}  kernel"]
+    for name, calls, tot, avg, pct in rows:
+        # top_kernels durations are in microseconds
+        out.append(f"{calls:6d} {avg:10.2f} {tot:11.1f} {pct:6.2f}  {name}")
+    return "\n".join(out)
+
+
+def _pmc_rows(path: str, counter: str):
+    import csv
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                rows.append((r.get("Kernel_Name", ""), float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows in {path}")
+    return rows
+
+
+def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel_substr, copy_bytes):
+    """HBM bytes per launch of the kernels whose name contains kernel_substr:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) averaged over its dispatches,
+    each scaled by (known bytes / counter reading) of a plain device copy."""
+    def mean_of(path, counter, pick):
+        vals = [v for n, v in _pmc_rows(path, counter) if pick(n)]
+        if not vals:
+            raise SystemExit(f"no {counter} dispatch of the selected kernel in {path}")
+        return float(np.mean(vals)), len(vals)
+
+    fk, nf = mean_of(fetch_csv, "FETCH_SIZE", lambda n: kernel_substr in n)
+    wk, nw = mean_of(write_csv, "WRITE_SIZE", lambda n: kernel_substr in n)
+    # the copy probe's copy is its largest dispatch
+    cf = max(v for _, v in _pmc_rows(copy_fetch_csv, "FETCH_SIZE"))
+    cw = max(v for _, v in _pmc_rows(copy_write_csv, "WRITE_SIZE"))
+    kib = copy_bytes / 1024.0
+    ff, fw = kib / cf, kib / cw
+    traffic = (fk * ff + wk * fw) * 1024.0
+    return "\n".join([
+        f"kernel_match: {kernel_substr}",
+        f"fetch_kib_per_dispatch: {fk:.1f}   (mean of {nf} dispatches)",
+        f"write_kib_per_dispatch: {wk:.1f}   (mean of {nw} dispatches)",
+        f"copy_bytes: {copy_bytes}",
+        f"copy_fetch_kib: {cf:.1f}",
+        f"copy_write_kib: {cw:.1f}",
+        f"fetch_factor: {ff:.4f}",
+        f"write_factor: {fw:.4f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        f"source_sha256: {gemm_source_hash()}",
+    ])
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,14 +209,26 @@ def main(argv=None) -> int:
                     help="GEMM accumulation: exact products with fp32 sums (default) or the FP8 "
                          "instructions' own accumulation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=256)
+    ap.add_argument("--cpu-sample-rows", type=int, default=2048)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="print a rocprofv3 kernel-trace summary and exit")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                                "COPY_WRITE_CSV"),
+                    help="print the calibrated HBM traffic of the GEMM kernel and exit")
+    ap.add_argument("--kernel-match", default="k_gemm_", help="kernel-name substring for --summarize-traffic")
     args = ap.parse_args(argv)
 
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return 0
+    if args.summarize_traffic:
+        print(summarize_traffic(*args.summarize_traffic, args.kernel_match, COPY_PROBE_BYTES))
+        return 0
+
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this path has no multi-GPU mode (sharding is described in "
-              "DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: this path has no multi-GPU mode (each GPU would run the same "
+              "kernels on its own shard); run with --gpus 1", file=sys.stderr)
         return 2
 
     import torch
@@ -119,7 +242,7 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream()
 
     if args.copy_probe:
-        n = 256 << 20
+        n = COPY_PROBE_BYTES
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         for _ in range(5):
@@ -157,6 +280,13 @@ def main(argv=None) -> int:
         sets.append((x, w, xq, wq, sx, sw, out))
     wsx = torch.empty(max(1, fb.fp8_quantize_workspace_bytes(M, K, wl.x_gran)), dtype=torch.uint8, device=dev)
     wsw = torch.empty(max(1, fb.fp8_quantize_workspace_bytes(N, K, wl.w_gran)), dtype=torch.uint8, device=dev)
+    # Decode: the weights are quantized once (setup), the step quantizes the
+    # activations and runs the GEMM.
+    w_in_step = wl.M > 32
+    if not w_in_step:
+        for x, w, xq, wq, sx, sw, out in sets:
+            fb.fp8_quantize(w, wl.w_fmt, wl.w_gran, q=wq, scales=sw, workspace=wsw, stream=stream)
+        torch.cuda.synchronize()
 
     def step(i, ev=None):
         x, w, xq, wq, sx, sw, out = sets[i % R]
@@ -165,7 +295,8 @@ def main(argv=None) -> int:
         fb.fp8_quantize(x, wl.x_fmt, wl.x_gran, q=xq, scales=sx, workspace=wsx, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        fb.fp8_quantize(w, wl.w_fmt, wl.w_gran, q=wq, scales=sw, workspace=wsw, stream=stream)
+        if w_in_step:
+            fb.fp8_quantize(w, wl.w_fmt, wl.w_gran, q=wq, scales=sw, workspace=wsw, stream=stream)
         if ev is not None:
             ev[2].record(stream)
         fb.fp8_gemm_blockscaled(xq, wl.x_fmt, wl.x_gran, sx, wq, wl.w_fmt, wl.w_gran, sw, wl.out_dtype,
@@ -199,19 +330,20 @@ def main(argv=None) -> int:
     value = flops / (ms_step * 1e-3) / 1e12
     gemm_tflops = flops / (gm_ms * 1e-3) / 1e12
     qx_gbs = quant_bytes(wl, "x") / (qx_ms * 1e-3) / 1e9
-    qw_gbs = quant_bytes(wl, "w") / (qw_ms * 1e-3) / 1e9
+    qw_gbs = quant_bytes(wl, "w") / (qw_ms * 1e-3) / 1e9 if w_in_step else None
     gemm_hbm_gbs = gemm_bytes(wl) / (gm_ms * 1e-3) / 1e9
 
     skinny = wl.M <= 32
+    traffic = read_traffic(wl.name, args.accum)
     # The default accumulation runs on the bf16 matrix cores (exact products of
     # the expanded codes, fp32 sums): its own dtype's dense peak is 2.5 PFLOP/s.
     peak_mfma = PEAK_FP8_TFLOPS if accum == fb.ACCUM_NATIVE else PEAK_BF16_TFLOPS
     if skinny:
         roof = {"bound": "hbm", "achieved": round(gemm_hbm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gemm_hbm_gbs / PEAK_HBM_GBS, 4), "traffic": None}
+                "frac": round(gemm_hbm_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
         roof = {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak_mfma, "unit": "TFLOP/s",
-                "frac": round(gemm_tflops / peak_mfma, 4), "traffic": None}
+                "frac": round(gemm_tflops / peak_mfma, 4), "traffic": traffic}
 
     result = {
         "metric": METRIC,
@@ -230,7 +362,8 @@ def main(argv=None) -> int:
         "config": {"workload": f"{wl.name}: M={M} N={N} K={K}, X 1x128 tiles, W 128x128 blocks, "
                                f"E4M3, fp32 scales, bf16 out" if wl.name == "c3_deepseek_block" else
                                f"{wl.name}: M={M} N={N} K={K}",
-                   "step": "quantize X + quantize W + GEMM", "rotated_input_sets": R,
+                   "step": "quantize X + quantize W + GEMM" if w_in_step else
+                           "quantize X + GEMM (W quantized once in setup)", "rotated_input_sets": R,
                    "accumulation": args.accum},
         "roofline": roof,
         "kernels": {
@@ -239,8 +372,9 @@ def main(argv=None) -> int:
             "gemm_algorithmic_gbs": round(gemm_hbm_gbs, 1),
             "quantize_x_ms": round(qx_ms, 4), "quantize_x_gbs": round(qx_gbs, 1),
             "quantize_x_frac_hbm": round(qx_gbs / PEAK_HBM_GBS, 4),
-            "quantize_w_ms": round(qw_ms, 4), "quantize_w_gbs": round(qw_gbs, 1),
-            "quantize_w_frac_hbm": round(qw_gbs / PEAK_HBM_GBS, 4),
+            "quantize_w_ms": round(qw_ms, 4) if w_in_step else None,
+            "quantize_w_gbs": round(qw_gbs, 1) if w_in_step else None,
+            "quantize_w_frac_hbm": round(qw_gbs / PEAK_HBM_GBS, 4) if w_in_step else None,
         },
         "wall_s_timed": round(wall, 4),
     }

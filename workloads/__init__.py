@@ -13,7 +13,7 @@ paragraph after the qdq listing), weights "tightly clustered around zero"
 orders of magnitude for the E5M2 operand (page "The FP8 Family", E5M2 row of
 the format table).
 
-Generator recipe (fixed, documented in the design doc as well):
+Generator recipe (fixed):
   rng = numpy.random.default_rng(seed)            # PCG64
   X   = rng.standard_normal((M, K), float32)
   if outliers: cols = rng.choice(K, n, replace=False); X[:, cols] *= factor
