@@ -209,7 +209,7 @@ def main(argv=None) -> int:
                     help="GEMM accumulation: exact products with fp32 sums (default) or the FP8 "
                          "instructions' own accumulation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=2048)
+    ap.add_argument("--cpu-sample-rows", type=int, default=4096)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="print a rocprofv3 kernel-trace summary and exit")
