@@ -79,7 +79,6 @@ __device__ __forceinline__ void tile_coords(int64_t bid, int64_t ntm, int64_t nt
   tn = in_g / gm;
 }
 
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // Chunk swizzle of LDS tile row r (see the layout note above).
 __device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -93,6 +92,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2][(TBM + TBN) * TBK];
   __shared__ __attribute__((aligned(16))) float s_x[2][TBM];                     // MODE_PROMOTE: sA[m, kb]
   __shared__ __attribute__((aligned(16))) uint32_t s_e[2][TBM + TBN];            // MODE_MX: 4 scale bytes per row
+  __shared__ __attribute__((aligned(16))) float s_w[2][64];                      // MODE_PROMOTE: sB[n/128, kb]
 
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t ntm = (M + TBM - 1) / TBM, ntn = (N + TBN - 1) / TBN;
@@ -114,18 +114,24 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // 8 rows (1 KiB) per load instruction; wave w issues instructions
   // [w*LPW, w*LPW + LPW).  Lane q lands in row 8u + q/8, stored chunk q%8,
   // which holds logical chunk (q%8) ^ lds_swz(row).
-  // Row 8x + q/8 has lds_swz = (q/8) ^ (x & 1), so a lane's offset is one of
-  // two per-lane values plus a wave-uniform row shift.
+  // Row 8x + q/8 has lds_swz = (q/8) ^ (x & 1), so a lane's offset inside its
+  // 8-row block is one of two per-lane values; the block itself is selected
+  // by a descriptor that starts at its first row and ends after the tile's
+  // last valid row (scalar arithmetic, no per-block vector registers).
   const int q8 = lane >> 3;
   const int goff_even = q8 * (int)K + (((lane & 7) ^ q8) << 4);
   const int goff_odd = q8 * (int)K + (((lane & 7) ^ q8 ^ 1) << 4);
-  auto goff = [&](int x) {           // x: 8-row block index inside its own tile
-    return ((x & 1) ? goff_odd : goff_even) + 8 * x * (int)K;
+  auto block_rsrc = [&](const uint8_t* base, int64_t rows, int x) {  // x: 8-row block inside its tile
+    const int64_t left = rows - 8 * x;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base + 8 * x * K), 0,
+                                             (int)(left > 0 ? left * K : 0), kBufferFlags);
   };
+  const uint8_t* a_base = p.a + m0 * K;
+  const uint8_t* b_base = p.b + n0 * K;
 
   // Scale descriptors (same row ranges) and per-lane offsets of the staged scales.
   const int64_t kq = K / 32;
-  __amdgpu_buffer_rsrc_t rssa = rsa, rssb = rsb;
+  __amdgpu_buffer_rsrc_t rssa = block_rsrc(a_base, rows_a, 0), rssb = block_rsrc(b_base, rows_b, 0);
   if constexpr (MODE == MODE_PROMOTE)
     rssa = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(reinterpret_cast<const float*>(p.sa) + m0 * nkb), 0,
                                              (int)(rows_a * nkb * 4), kBufferFlags);
@@ -137,34 +143,36 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   }
   const float* swb = reinterpret_cast<const float*>(p.sb);
   const float* sxa = reinterpret_cast<const float*>(p.sa);
+  // W block scales: blocks n0/128 .. (n0 + rows_b - 1)/128 (MODE_PROMOTE)
+  const int64_t wblk0 = n0 / 128, wblks = (n0 + rows_b + 127) / 128 - wblk0;
+  const __amdgpu_buffer_rsrc_t rssw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(swb + wblk0 * nkb), 0, (int)(MODE == MODE_PROMOTE ? wblks * nkb * 4 : 0), kBufferFlags);
 
   auto issue_loads = [&](int kb, int buf) {
     const int kk = kb * 128;
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
       const int x = w * LPW + u;       // 8-row block of the A+B list (wave-uniform)
-      if (8 * x < TBM)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, LDS_PTR(&smem[buf][8 * x * 128]), 16, goff(x) + kk, 0, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, LDS_PTR(&smem[buf][8 * x * 128]), 16, goff(x - TBM / 8) + kk,
-                                                 0, 0, 0);
+      const int off = ((x & 1) ? goff_odd : goff_even) + kk;
+      const bool is_a = 8 * x < TBM;   // wave-uniform: scalar selects, no branch
+      dma_to_lds<16>(block_rsrc(is_a ? a_base : b_base, is_a ? rows_a : rows_b, is_a ? x : x - TBM / 8),
+                     lds_addr(&smem[buf][8 * x * 128]), off);
     }
     // scales: one 4-byte load per lane, 64 rows per wave; A rows first, then B rows (MX)
     if constexpr (MODE == MODE_PROMOTE) {
+      // the (up to TBN/128 + 1) W block scales of this tile's columns; lanes past them read zeros
+      if (w == NW - 1) dma_to_lds<4>(rssw, lds_addr(&s_w[buf][0]), (lane * nkb + kb) * 4);
 #pragma unroll
       for (int v = w; v < TBM / 64; v += NW)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rssa, LDS_PTR(&s_x[buf][64 * v]), 4, ((64 * v + lane) * nkb + kb) * 4,
-                                                 0, 0, 0);
+        dma_to_lds<4>(rssa, lds_addr(&s_x[buf][64 * v]), ((64 * v + lane) * nkb + kb) * 4);
     }
     if constexpr (MODE == MODE_MX) {
 #pragma unroll
       for (int v = w; v < (TBM + TBN) / 64; v += NW) {
         if (v < TBM / 64)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rssa, LDS_PTR(&s_e[buf][64 * v]), 4,
-                                                   (int)((64 * v + lane) * kq + kb * 4), 0, 0, 0);
+          dma_to_lds<4>(rssa, lds_addr(&s_e[buf][64 * v]), (int)((64 * v + lane) * kq + kb * 4));
         else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rssb, LDS_PTR(&s_e[buf][64 * v]), 4,
-                                                   (int)((64 * v - TBM + lane) * kq + kb * 4), 0, 0, 0);
+          dma_to_lds<4>(rssb, lds_addr(&s_e[buf][64 * v]), (int)((64 * v - TBM + lane) * kq + kb * 4));
       }
     }
   };
@@ -200,7 +208,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
     auto lds16 = [&](const uint8_t* base, int off) { return *reinterpret_cast<const u32x4*>(base + off); };
 
     float swv = 1.0f;
-    if constexpr (MODE == MODE_PROMOTE) swv = swb[nblk * nkb + kb];
+    if constexpr (MODE == MODE_PROMOTE) swv = s_w[buf][nblk - wblk0];
 
     if constexpr (PATH == PATH_FAST) {
       v8i fb[4];
@@ -249,9 +257,9 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       }
       if constexpr (MODE == MODE_PROMOTE) {
         // Software-pipelined order: A tile i+1 is read and converted while
-        // tile i multiplies; each N tile is a chain of four dependent MFMAs
-        // (the 128-K partial P), and chain j-1 is promoted into the fp32
-        // accumulator while chain j runs.
+        // tile i multiplies; each N tile's 128-K partial P is a chain of four
+        // MFMAs, and the four chains of a tile row are interleaved before P
+        // is promoted into the fp32 accumulator.
         u32x4 n0 = lds16(sa_, a_row0 * 128 + c0), n1 = lds16(sa_, a_row0 * 128 + c1);
         v8bf xa[4];
         xa[0] = cvt8<AF>(n0.x, n0.y, 1.0f);
@@ -267,26 +275,37 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
           }
           const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * 128 + 16 * i + 4 * g]);
           const v4f sc = {sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};
-          v4f prev = {0.0f, 0.0f, 0.0f, 0.0f};
+          // Four independent chains (one per N tile), interleaved so that
+          // no MFMA waits on the previous one; the wave's priority is raised
+          // while it issues them so that a co-resident wave's VALU work fills
+          // the gaps instead of delaying the matrix cores.
+          __builtin_amdgcn_s_setprio(1);
+          v4f pp[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            v4f pp = mfma_bf16(xa[0], xb[j][0], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-            pp = mfma_bf16(xa[1], xb[j][1], pp);
-            pp = mfma_bf16(xa[2], xb[j][2], pp);
-            pp = mfma_bf16(xa[3], xb[j][3], pp);
-            if (j > 0) {
+          for (int j = 0; j < 4; ++j) pp[j] = mfma_bf16(xa[0], xb[j][0], v4f{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
-              for (int q = 0; q < 4; ++q) acc[i][j - 1][q] = __builtin_fmaf(prev[q], sc[q], acc[i][j - 1][q]);
-            }
-            prev = pp;
-          }
+          for (int s = 1; s < 4; ++s)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[i][3][q] = __builtin_fmaf(prev[q], sc[q], acc[i][3][q]);
+            for (int j = 0; j < 4; ++j) pp[j] = mfma_bf16(xa[s], xb[j][s], pp[j]);
+          __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(pp[j][q], sc[q], acc[i][j][q]);
           if (i + 1 < 8) {
             xa[0] = cvt8<AF>(n0.x, n0.y, 1.0f);
             xa[1] = cvt8<AF>(n0.z, n0.w, 1.0f);
             xa[2] = cvt8<AF>(n1.x, n1.y, 1.0f);
             xa[3] = cvt8<AF>(n1.z, n1.w, 1.0f);
+          }
+          // Issue order for the scheduler: the two LDS reads of the next A
+          // tile first, then each MFMA followed by two VALU instructions
+          // (promotion FMAs and the next tile's conversions).
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+          for (int z = 0; z < 16; ++z) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
           }
         }
       } else {

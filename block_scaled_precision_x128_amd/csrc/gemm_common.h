@@ -24,6 +24,32 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, int vo
   return u32x4{(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
 }
 
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
+
+// Per-lane load of SIZE (16 or 4) bytes at buffer offset voff, written by the
+// load unit straight into LDS at lds_base + SIZE * lane (offsets at or past
+// the descriptor's size write zeros).  Issued as assembly on purpose: the
+// compiler cannot tell which LDS stage such a load targets, so for its own
+// load-to-LDS instruction it waits for every one in flight before any later
+// LDS read, which would serialize a double-buffered pipeline.  The caller
+// orders these loads with s_waitcnt vmcnt(0) and a workgroup barrier before
+// any wave reads the stage they fill.  M0 is written here and every load to
+// LDS in this library goes through this function, so no compiler-set M0 value
+// is relied on across it.
+template <int SIZE>
+__device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t lds_base, int voff) {
+  static_assert(SIZE == 16 || SIZE == 4, "16- or 4-byte loads");
+  if constexpr (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(lds_base)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(lds_base)
+                 : "memory");
+}
+
 template <int AF, int BF>
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, sa, 0, sb);
