@@ -6,6 +6,7 @@ already resident in HBM:
     quantize X (bf16 -> E4M3, fp32 scale per 1x128 tile)
     quantize W (bf16 -> E4M3, fp32 scale per 128x128 block)
     GEMM  out = sum_kb sX[m,kb] sW[n/128,kb] (X_kb @ W_kb^T), bf16 out
+    dequantize X (the activation round trip, codes -> bf16)
 on the DeepSeek-V3-style block-scaled workload M=4096, N=7168, K=7168.
 `value` is 2*M*N*K / (time per step) in TFLOP/s.  The dominant kernel (the
 GEMM) is also timed on its own with HIP events on the launch stream, and
@@ -65,6 +66,12 @@ def quant_bytes(wl, operand: str) -> int:
     gran = wl.x_gran if operand == "x" else wl.w_gran
     in_b = 2 if wl.in_dtype == workloads.DT_BF16 else 4
     return rows * cols * (in_b + 1) + scale_bytes(gran, rows, cols)
+
+
+def dequant_bytes(wl) -> int:
+    """Algorithmic bytes of dequantizing X: codes and scales read, values written in the input dtype."""
+    out_b = 2 if wl.in_dtype == workloads.DT_BF16 else 4
+    return wl.M * wl.K * (1 + out_b) + scale_bytes(wl.x_gran, wl.M, wl.K)
 
 
 def gemm_bytes(wl) -> int:
@@ -264,7 +271,7 @@ def main(argv=None) -> int:
     x0, w0 = to_dev(xs_np), to_dev(ws_np)
     del xs_np, ws_np
     in_b = 2 if wl.in_dtype == workloads.DT_BF16 else 4
-    set_bytes = (M + N) * K * (in_b + 1) + M * N * 4
+    set_bytes = (M + N) * K * (in_b + 1) + M * N * 4 + M * K * in_b
     R = args.sets or max(2, int(np.ceil(1.2e9 / set_bytes)))
     sets = []
     for r in range(R):
@@ -277,19 +284,20 @@ def main(argv=None) -> int:
         sw = torch.empty(fb.scale_shape(wl.w_gran, N, K), dtype=sdt(wl.w_gran), device=dev)
         out = torch.empty((M, N), dtype=torch.bfloat16 if wl.out_dtype == fb.DT_BF16 else torch.float32,
                           device=dev)
-        sets.append((x, w, xq, wq, sx, sw, out))
+        xr = torch.empty_like(x)   # dequantized X
+        sets.append((x, w, xq, wq, sx, sw, out, xr))
     wsx = torch.empty(max(1, fb.fp8_quantize_workspace_bytes(M, K, wl.x_gran)), dtype=torch.uint8, device=dev)
     wsw = torch.empty(max(1, fb.fp8_quantize_workspace_bytes(N, K, wl.w_gran)), dtype=torch.uint8, device=dev)
     # Decode: the weights are quantized once (setup), the step quantizes the
     # activations and runs the GEMM.
     w_in_step = wl.M > 32
     if not w_in_step:
-        for x, w, xq, wq, sx, sw, out in sets:
+        for x, w, xq, wq, sx, sw, out, xr in sets:
             fb.fp8_quantize(w, wl.w_fmt, wl.w_gran, q=wq, scales=sw, workspace=wsw, stream=stream)
         torch.cuda.synchronize()
 
     def step(i, ev=None):
-        x, w, xq, wq, sx, sw, out = sets[i % R]
+        x, w, xq, wq, sx, sw, out, xr = sets[i % R]
         if ev is not None:
             ev[0].record(stream)
         fb.fp8_quantize(x, wl.x_fmt, wl.x_gran, q=xq, scales=sx, workspace=wsx, stream=stream)
@@ -303,13 +311,16 @@ def main(argv=None) -> int:
                                 out=out, accum=accum, stream=stream)
         if ev is not None:
             ev[3].record(stream)
+        fb.fp8_dequantize(xq, sx, wl.x_fmt, wl.x_gran, wl.in_dtype, y=xr, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     # timed region: whole steps, bracketed by synchronizations
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -325,6 +336,8 @@ def main(argv=None) -> int:
     qx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     qw_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     gm_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    dq_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
+    dq_gbs = dequant_bytes(wl) / (dq_ms * 1e-3) / 1e9
 
     flops = 2.0 * M * N * K
     value = flops / (ms_step * 1e-3) / 1e12
@@ -362,8 +375,9 @@ def main(argv=None) -> int:
         "config": {"workload": f"{wl.name}: M={M} N={N} K={K}, X 1x128 tiles, W 128x128 blocks, "
                                f"E4M3, fp32 scales, bf16 out" if wl.name == "c3_deepseek_block" else
                                f"{wl.name}: M={M} N={N} K={K}",
-                   "step": "quantize X + quantize W + GEMM" if w_in_step else
-                           "quantize X + GEMM (W quantized once in setup)", "rotated_input_sets": R,
+                   "step": "quantize X + quantize W + GEMM + dequantize X" if w_in_step else
+                           "quantize X + GEMM + dequantize X (W quantized once in setup)",
+                   "rotated_input_sets": R,
                    "accumulation": args.accum},
         "roofline": roof,
         "kernels": {
@@ -375,6 +389,8 @@ def main(argv=None) -> int:
             "quantize_w_ms": round(qw_ms, 4) if w_in_step else None,
             "quantize_w_gbs": round(qw_gbs, 1) if w_in_step else None,
             "quantize_w_frac_hbm": round(qw_gbs / PEAK_HBM_GBS, 4) if w_in_step else None,
+            "dequantize_x_ms": round(dq_ms, 4), "dequantize_x_gbs": round(dq_gbs, 1),
+            "dequantize_x_frac_hbm": round(dq_gbs / PEAK_HBM_GBS, 4),
         },
         "wall_s_timed": round(wall, 4),
     }

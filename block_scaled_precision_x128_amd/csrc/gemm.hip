@@ -80,8 +80,6 @@ __device__ __forceinline__ void tile_coords(int64_t bid, int64_t ntm, int64_t nt
 }
 
 
-// Chunk swizzle of LDS tile row r (see the layout note above).
-__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 template <int AF, int BF, int MODE, int ODT, int PATH, int WMW, int WNW>
 __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
@@ -105,11 +103,6 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   const int64_t rows_a = (M - m0) < TBM ? (M - m0) : TBM;
   const int64_t rows_b = (N - n0) < TBN ? (N - n0) : TBN;
 
-  // Operand descriptors start at the tile's first row and end after its last valid row.
-  const __amdgpu_buffer_rsrc_t rsa =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a + m0 * K), 0, (int)(rows_a * K), kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rsb =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.b + n0 * K), 0, (int)(rows_b * K), kBufferFlags);
   // The TBM A rows and TBN B rows of a K step form one list of LDS rows,
   // 8 rows (1 KiB) per load instruction; wave w issues instructions
   // [w*LPW, w*LPW + LPW).  Lane q lands in row 8u + q/8, stored chunk q%8,
@@ -122,9 +115,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   const int goff_even = q8 * (int)K + (((lane & 7) ^ q8) << 4);
   const int goff_odd = q8 * (int)K + (((lane & 7) ^ q8 ^ 1) << 4);
   auto block_rsrc = [&](const uint8_t* base, int64_t rows, int x) {  // x: 8-row block inside its tile
-    const int64_t left = rows - 8 * x;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base + 8 * x * K), 0,
-                                             (int)(left > 0 ? left * K : 0), kBufferFlags);
+    return uniform_rsrc(base + 8 * x * K, (rows - 8 * x) * K);
   };
   const uint8_t* a_base = p.a + m0 * K;
   const uint8_t* b_base = p.b + n0 * K;
@@ -133,20 +124,16 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   const int64_t kq = K / 32;
   __amdgpu_buffer_rsrc_t rssa = block_rsrc(a_base, rows_a, 0), rssb = block_rsrc(b_base, rows_b, 0);
   if constexpr (MODE == MODE_PROMOTE)
-    rssa = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(reinterpret_cast<const float*>(p.sa) + m0 * nkb), 0,
-                                             (int)(rows_a * nkb * 4), kBufferFlags);
+    rssa = uniform_rsrc(reinterpret_cast<const float*>(p.sa) + m0 * nkb, rows_a * nkb * 4);
   if constexpr (MODE == MODE_MX) {
-    rssa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.sa) + m0 * kq), 0,
-                                             (int)(rows_a * kq), kBufferFlags);
-    rssb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(p.sb) + n0 * kq), 0,
-                                             (int)(rows_b * kq), kBufferFlags);
+    rssa = uniform_rsrc(reinterpret_cast<const uint8_t*>(p.sa) + m0 * kq, rows_a * kq);
+    rssb = uniform_rsrc(reinterpret_cast<const uint8_t*>(p.sb) + n0 * kq, rows_b * kq);
   }
   const float* swb = reinterpret_cast<const float*>(p.sb);
   const float* sxa = reinterpret_cast<const float*>(p.sa);
   // W block scales: blocks n0/128 .. (n0 + rows_b - 1)/128 (MODE_PROMOTE)
   const int64_t wblk0 = n0 / 128, wblks = (n0 + rows_b + 127) / 128 - wblk0;
-  const __amdgpu_buffer_rsrc_t rssw = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(swb + wblk0 * nkb), 0, (int)(MODE == MODE_PROMOTE ? wblks * nkb * 4 : 0), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rssw = uniform_rsrc(swb + wblk0 * nkb, MODE == MODE_PROMOTE ? wblks * nkb * 4 : 0);
 
   auto issue_loads = [&](int kb, int buf) {
     const int kk = kb * 128;

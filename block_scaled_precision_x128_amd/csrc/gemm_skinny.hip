@@ -19,32 +19,42 @@
 //    each wave computes all T = ceil(R / 16) column tiles of its range, so an
 //    X fragment (from L2: X is small) is fetched once per workgroup and used
 //    T times, and the extra traffic through the unit is |X| per workgroup.
-//  * Each wave keeps two 128-K steps of loads in flight in statically named
-//    register sets.  Steps past the wave's range load through an out-of-range
-//    offset (zeros, no memory traffic) and are not computed, so there are no
-//    data-dependent branches around loads and the compiler's waits count
-//    exactly the loads of older steps.
+//  * Full-line loads.  W and X reach LDS through loads that write LDS
+//    directly, each instruction fetching 8 whole 128-byte rows (a load of the
+//    matrix-core fragments straight into registers fetches 16 half rows per
+//    instruction, and the unit's request rate, not its byte rate, then bounds
+//    the stream).  Fragments are read back from LDS in the matrix-core
+//    layout, through the same conflict-free chunk swizzle as the tiled kernel.
+//  * Each wave owns two LDS stages: the loads of step k+1 are in flight while
+//    step k is computed.  Steps past the wave's range load zeros (no memory
+//    traffic) and are not computed, so every step issues the same loads and
+//    a fixed s_waitcnt count leaves exactly one step's loads in flight.
 //  * The S partial tiles are added in LDS at the end.
 #include "gemm_common.h"
 
 namespace fp8blk {
 
-// Registers of one 128-K step.
+// LDS footprint of one wave's stage (bytes): W rows, X rows, then scales.
 template <int MODE, int MT, int T>
-struct SkinnyStep {
-  u32x4 b[T][2];       // W fragment pieces, per column tile
-  u32x4 a[MT][2];      // X fragment pieces, per 16-row tile of X
-  float sx[MT][4];     // promotion: X scales of the lane's 4 rows
-  uint32_t eb[T];      // MX: W scale byte of the lane's 32-K block
-  uint32_t ea[MT];     // MX: X scale byte
+struct SkinnyStage {
+  static constexpr int kW = 16 * T * 128;          // W tile rows (128 K bytes each)
+  static constexpr int kX = 16 * MT * 128;         // X tile rows
+  static constexpr int kScale = MODE == MODE_PROMOTE ? 2 * 256 : (MODE == MODE_MX ? 3 * 256 : 0);
+  static constexpr int kBytes = kW + kX + kScale;
+  // loads issued per step (every one is issued, out-of-range ones read zeros)
+  static constexpr int kLoads = 2 * T + 2 * MT + (MODE == MODE_PROMOTE ? 2 : (MODE == MODE_MX ? 3 : 0));
 };
 
 // R (W rows per workgroup) <= 16 * T <= 112, so a workgroup's rows touch at
-// most two 128-row W scale blocks.
+// most two 128-row W scale blocks and their MX scale words fit two 64-lane loads.
 template <int AF, int BF, int MODE, int ODT, int PATH, int MT, int T, int S>
 __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
   static_assert(16 * T <= 112, "a workgroup's rows must touch at most two 128-row scale blocks");
-  __shared__ __attribute__((aligned(16))) float red[S][MT * T][64][4];
+  using St = SkinnyStage<MODE, MT, T>;
+  static_assert(2 * St::kLoads <= 63, "loads in flight must fit the vmcnt counter");
+  static_assert(MT * T * 64 * 16 <= 2 * St::kBytes, "partial tiles must fit in the wave's stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[S][2][St::kBytes];
+
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t n0 = (int64_t)blockIdx.x * R;
   if (n0 >= N) return;  // whole workgroup: no barrier has been reached
@@ -52,29 +62,65 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), g = lane >> 4;
   const int kb0 = (int)((int64_t)w * nkb / S), kb1 = (int)((int64_t)(w + 1) * nkb / S);
   const int64_t rows = (N - n0) < R ? (N - n0) : R;
+  const int64_t kq = K / 32;
 
-  // Byte offsets of the lane's two 16-byte pieces inside a 128-K step:
-  // exact path, 32 consecutive bytes (one MX block) per lane; fast path, the
-  // FP8 instruction's K order.
-  const int o0 = PATH == PATH_EXACT ? 32 * g : 16 * g;
-  const int o1 = PATH == PATH_EXACT ? 32 * g + 16 : 64 + 16 * g;
-  const __amdgpu_buffer_rsrc_t rw =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.b + n0 * K), 0, (int)(rows * K), kBufferFlags);
-  const __amdgpu_buffer_rsrc_t rx =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.a), 0, (int)(M * K), kBufferFlags);
-  const int lrow = (lane & 15) * (int)K;
-  const int tile_stride = 16 * (int)K;
-
+  // Loads into LDS, 8 full 128-byte rows per instruction: lane q takes row
+  // q/8 of its 8-row block and stored chunk q%8, i.e. logical chunk
+  // (q%8) ^ lds_swz(row); lds_swz(8u + q/8) = (q/8) ^ (u & 1).
+  const int q8 = lane >> 3;
+  const int off_even = q8 * (int)K + (((lane & 7) ^ q8) << 4);
+  const int off_odd = q8 * (int)K + (((lane & 7) ^ q8 ^ 1) << 4);
+  auto rsrc = [&](const void* base, int64_t bytes) { return uniform_rsrc(base, bytes); };
+  const uint8_t* wbase = p.b + n0 * K;
   const float* sxa = reinterpret_cast<const float*>(p.sa);
   const float* swb = reinterpret_cast<const float*>(p.sb);
-  const uint8_t* eab = reinterpret_cast<const uint8_t*>(p.sa);
-  const uint8_t* ebb = reinterpret_cast<const uint8_t*>(p.sb);
-  const int64_t kq = K / 32;
-  // Promotion: the W scale of a lane's column is one of two per-step values
-  // (blocks blo and blo + 1, clamped to the last block).
   const int64_t blo = n0 / 128, nblk = (N + 127) / 128;
-  const float* sw_lo = swb + blo * nkb;
-  const float* sw_hi = swb + (blo + 1 < nblk ? blo + 1 : blo) * nkb;
+  // descriptors of the per-step scale loads
+  __amdgpu_buffer_rsrc_t rs_sx = rsrc(p.sa, 0), rs_sw = rsrc(p.sb, 0), rs_ex = rsrc(p.sa, 0), rs_ew = rsrc(p.sb, 0);
+  if constexpr (MODE == MODE_PROMOTE) {
+    rs_sx = rsrc(sxa, M * nkb * 4);                                    // sA[m, kb], lanes m < M
+    rs_sw = rsrc(swb + blo * nkb, ((blo + 1 < nblk) ? 2 : 1) * nkb * 4);  // sB[blo + l, kb], l < 2
+  }
+  if constexpr (MODE == MODE_MX) {
+    rs_ex = rsrc(p.sa, M * kq);                                        // 4 UE8M0 bytes of row m, step kb
+    rs_ew = rsrc(reinterpret_cast<const uint8_t*>(p.sb) + n0 * kq, rows * kq);
+  }
+
+  auto issue = [&](int k, int stage) {
+    const bool valid = k < kb1;
+    const int kk = valid ? k * 128 : kOutOfRange;
+    uint8_t* st = &lds[w][stage][0];
+#pragma unroll
+    for (int u = 0; u < 2 * T; ++u) {
+      const int64_t left = rows - 8 * u;
+      dma_to_lds<16>(rsrc(wbase + 8 * u * K, left * K), lds_addr(st + 8 * u * 128), ((u & 1) ? off_odd : off_even) + kk);
+    }
+#pragma unroll
+    for (int u = 0; u < 2 * MT; ++u) {
+      const int64_t left = M - 8 * u;
+      dma_to_lds<16>(rsrc(p.a + 8 * u * K, left * K), lds_addr(st + St::kW + 8 * u * 128),
+                     ((u & 1) ? off_odd : off_even) + kk);
+    }
+    uint8_t* sc = st + St::kW + St::kX;
+    if constexpr (MODE == MODE_PROMOTE) {
+      const int ks = valid ? k * 4 : kOutOfRange;
+      dma_to_lds<4>(rs_sx, lds_addr(sc), lane * nkb * 4 + ks);
+      dma_to_lds<4>(rs_sw, lds_addr(sc + 256), lane * nkb * 4 + ks);
+    }
+    if constexpr (MODE == MODE_MX) {
+      const int ks = valid ? k * 4 : kOutOfRange;
+      dma_to_lds<4>(rs_ex, lds_addr(sc), lane * (int)kq + ks);
+      dma_to_lds<4>(rs_ew, lds_addr(sc + 256), lane * (int)kq + ks);
+      dma_to_lds<4>(rs_ew, lds_addr(sc + 512), (64 + lane) * (int)kq + ks);
+    }
+  };
+
+  // Fragment reads: row r = 16 t + (lane & 15) of the stage, chunks (2g, 2g+1)
+  // on the exact path (K 32g..32g+31), (g, 4+g) on the fast path.
+  const int swz = lds_swz(lane & 15);
+  const int c0 = ((PATH == PATH_EXACT ? 2 * g : g) ^ swz) << 4;
+  const int c1 = ((PATH == PATH_EXACT ? 2 * g + 1 : 4 + g) ^ swz) << 4;
+  const int rlane = (lane & 15) * 128;
   bool hi[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) hi[t] = (n0 + 16 * t + (lane & 15)) / 128 > blo;
@@ -85,74 +131,55 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[mt][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto load = [&](SkinnyStep<MODE, MT, T>& Rg, int k) {
-    const bool valid = k < kb1;
-    const int kc = valid ? k : kb1 - 1;                  // scales: any valid step
-    const int kk = valid ? k * 128 : kOutOfRange;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      Rg.b[t][0] = buffer_load16(rw, lrow + t * tile_stride + kk + o0);
-      Rg.b[t][1] = buffer_load16(rw, lrow + t * tile_stride + kk + o1);
-    }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      Rg.a[mt][0] = buffer_load16(rx, lrow + mt * tile_stride + kk + o0);
-      Rg.a[mt][1] = buffer_load16(rx, lrow + mt * tile_stride + kk + o1);
-    }
-    if constexpr (MODE == MODE_PROMOTE) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          int64_t row = mt * 16 + 4 * g + r;
-          row = row < M ? row : M - 1;
-          Rg.sx[mt][r] = sxa[row * nkb + kc];
-        }
-    }
-    if constexpr (MODE == MODE_MX) {
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        int64_t n = n0 + 16 * t + (lane & 15);
-        n = n < N ? n : N - 1;
-        Rg.eb[t] = ebb[n * kq + kc * 4 + g];
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        int64_t row = mt * 16 + (lane & 15);
-        row = row < M ? row : M - 1;
-        Rg.ea[mt] = eab[row * kq + kc * 4 + g];
-      }
-    }
-  };
+  auto lds16 = [&](const uint8_t* b, int off) { return *reinterpret_cast<const u32x4*>(b + off); };
 
-  auto compute = [&](const SkinnyStep<MODE, MT, T>& Rg, int k) {
+  auto compute = [&](int stage) {
+    const uint8_t* st = &lds[w][stage][0];
+    const uint8_t* sc = st + St::kW + St::kX;
     float f_lo[MT][4], f_hi[MT][4];
     if constexpr (MODE == MODE_PROMOTE) {
-      const float s_lo = sw_lo[k], s_hi = sw_hi[k];
+      const float s_lo = reinterpret_cast<const float*>(sc + 256)[0];
+      const float s_hi = reinterpret_cast<const float*>(sc + 256)[1];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
+        const float4 sx4 = *reinterpret_cast<const float4*>(sc + (16 * mt + 4 * g) * 4);
+        const float sx[4] = {sx4.x, sx4.y, sx4.z, sx4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          f_lo[mt][r] = Rg.sx[mt][r] * s_lo;
-          f_hi[mt][r] = Rg.sx[mt][r] * s_hi;
+          f_lo[mt][r] = sx[r] * s_lo;
+          f_hi[mt][r] = sx[r] * s_hi;
         }
+      }
+    }
+    uint32_t ea[MT], eb[T];
+    if constexpr (MODE == MODE_MX) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        ea[mt] = (reinterpret_cast<const uint32_t*>(sc)[16 * mt + (lane & 15)] >> (8 * g)) & 0xffu;
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        eb[t] = (reinterpret_cast<const uint32_t*>(sc + 256)[16 * t + (lane & 15)] >> (8 * g)) & 0xffu;
     }
     if constexpr (PATH == PATH_FAST) {
       v8i fa[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) fa[mt] = join(Rg.a[mt][0], Rg.a[mt][1]);
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = St::kW + 16 * mt * 128 + rlane;
+        fa[mt] = join(lds16(st, r + c0), lds16(st, r + c1));
+      }
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const v8i fb = join(Rg.b[t][0], Rg.b[t][1]);
+        const int r = 16 * t * 128 + rlane;
+        const v8i fb = join(lds16(st, r + c0), lds16(st, r + c1));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           if constexpr (MODE == MODE_PROMOTE) {
             const v4f pr = mfma_fp8<AF, BF>(fa[mt], fb, v4f{0.0f, 0.0f, 0.0f, 0.0f}, (int)kUnitScale, (int)kUnitScale);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[mt][t][r] = __builtin_fmaf(pr[r], hi[t] ? f_hi[mt][r] : f_lo[mt][r], acc[mt][t][r]);
+            for (int q = 0; q < 4; ++q)
+              acc[mt][t][q] = __builtin_fmaf(pr[q], hi[t] ? f_hi[mt][q] : f_lo[mt][q], acc[mt][t][q]);
           } else if constexpr (MODE == MODE_MX) {
-            acc[mt][t] = mfma_fp8<AF, BF>(fa[mt], fb, acc[mt][t], (int)Rg.ea[mt], (int)Rg.eb[t]);
+            acc[mt][t] = mfma_fp8<AF, BF>(fa[mt], fb, acc[mt][t], (int)ea[mt], (int)eb[t]);
           } else {
             acc[mt][t] = mfma_fp8<AF, BF>(fa[mt], fb, acc[mt][t], (int)kUnitScale, (int)kUnitScale);
           }
@@ -163,20 +190,24 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
       v8bf xa[MT][4];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const float fsa = (MODE == MODE_MX) ? e8m0_to_f32(Rg.ea[mt]) : 1.0f;
-        xa[mt][0] = cvt8<AF>(Rg.a[mt][0].x, Rg.a[mt][0].y, fsa);
-        xa[mt][1] = cvt8<AF>(Rg.a[mt][0].z, Rg.a[mt][0].w, fsa);
-        xa[mt][2] = cvt8<AF>(Rg.a[mt][1].x, Rg.a[mt][1].y, fsa);
-        xa[mt][3] = cvt8<AF>(Rg.a[mt][1].z, Rg.a[mt][1].w, fsa);
+        const float fsa = (MODE == MODE_MX) ? e8m0_to_f32(ea[mt]) : 1.0f;
+        const int r = St::kW + 16 * mt * 128 + rlane;
+        const u32x4 d0 = lds16(st, r + c0), d1 = lds16(st, r + c1);
+        xa[mt][0] = cvt8<AF>(d0.x, d0.y, fsa);
+        xa[mt][1] = cvt8<AF>(d0.z, d0.w, fsa);
+        xa[mt][2] = cvt8<AF>(d1.x, d1.y, fsa);
+        xa[mt][3] = cvt8<AF>(d1.z, d1.w, fsa);
       }
 #pragma unroll
       for (int t = 0; t < T; ++t) {
-        const float fsb = (MODE == MODE_MX) ? e8m0_to_f32(Rg.eb[t]) : 1.0f;
+        const float fsb = (MODE == MODE_MX) ? e8m0_to_f32(eb[t]) : 1.0f;
+        const int r = 16 * t * 128 + rlane;
+        const u32x4 d0 = lds16(st, r + c0), d1 = lds16(st, r + c1);
         v8bf xb[4];
-        xb[0] = cvt8<BF>(Rg.b[t][0].x, Rg.b[t][0].y, fsb);
-        xb[1] = cvt8<BF>(Rg.b[t][0].z, Rg.b[t][0].w, fsb);
-        xb[2] = cvt8<BF>(Rg.b[t][1].x, Rg.b[t][1].y, fsb);
-        xb[3] = cvt8<BF>(Rg.b[t][1].z, Rg.b[t][1].w, fsb);
+        xb[0] = cvt8<BF>(d0.x, d0.y, fsb);
+        xb[1] = cvt8<BF>(d0.z, d0.w, fsb);
+        xb[2] = cvt8<BF>(d1.x, d1.y, fsb);
+        xb[3] = cvt8<BF>(d1.z, d1.w, fsb);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           if constexpr (MODE == MODE_PROMOTE) {
@@ -185,36 +216,40 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
             pp = mfma_bf16(xa[mt][2], xb[2], pp);
             pp = mfma_bf16(xa[mt][3], xb[3], pp);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[mt][t][r] = __builtin_fmaf(pp[r], hi[t] ? f_hi[mt][r] : f_lo[mt][r], acc[mt][t][r]);
+            for (int q = 0; q < 4; ++q)
+              acc[mt][t][q] = __builtin_fmaf(pp[q], hi[t] ? f_hi[mt][q] : f_lo[mt][q], acc[mt][t][q]);
           } else {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) acc[mt][t] = mfma_bf16(xa[mt][s], xb[s], acc[mt][t]);
+            for (int s4 = 0; s4 < 4; ++s4) acc[mt][t] = mfma_bf16(xa[mt][s4], xb[s4], acc[mt][t]);
           }
         }
       }
     }
   };
 
-  // Two register sets with static names (a runtime index would put them in
-  // scratch memory).
-  SkinnyStep<MODE, MT, T> r0, r1;
+  // Two stages per wave (private: no workgroup barrier in the loop).  The
+  // loads of step k+1 are issued before step k is computed; the explicit wait
+  // leaves exactly those kLoads loads in flight.  Steps past the wave's range
+  // load zeros and are not computed, so every iteration issues the same
+  // number of loads.
   if (kb0 < kb1) {
-    load(r0, kb0);
-    for (int k = kb0; k < kb1; k += 2) {
-      load(r1, k + 1);
-      compute(r0, k);
-      load(r0, k + 2);
-      if (k + 1 < kb1) compute(r1, k + 1);
+    issue(kb0, 0);
+    for (int k = kb0; k < kb1; ++k) {
+      issue(k + 1, (k + 1 - kb0) & 1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(St::kLoads) : "memory");
+      compute((k - kb0) & 1);
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last (zero) loads have landed
 
-  // Partial tiles of the S waves -> LDS -> one sum per output element.
+  // Partial tiles of the S waves -> LDS (each wave's own stages) -> one sum
+  // per output element.
+  float* red = reinterpret_cast<float*>(&lds[w][0][0]);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int t = 0; t < T; ++t)
-      *reinterpret_cast<float4*>(&red[w][mt * T + t][lane][0]) =
+      *reinterpret_cast<float4*>(&red[((mt * T + t) * 64 + lane) * 4]) =
           make_float4(acc[mt][t][0], acc[mt][t][1], acc[mt][t][2], acc[mt][t][3]);
   __syncthreads();
   for (int u = w; u < MT * T; u += S) {
@@ -227,7 +262,7 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
       const int64_t row = mt * 16 + 4 * g + r;
       float v = 0.0f;
 #pragma unroll
-      for (int s = 0; s < S; ++s) v += red[s][u][lane][r];
+      for (int s = 0; s < S; ++s) v += reinterpret_cast<const float*>(&lds[s][0][0])[(u * 64 + lane) * 4 + r];
       if (row >= M) continue;
       if constexpr (MODE == MODE_EPILOGUE) v = v * (sxa[p.a_per_row ? row : 0] * swb[p.b_per_row ? col : 0]);
       store_out<ODT>(p.out, row * N + col, v);
