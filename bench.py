@@ -8,10 +8,12 @@ already resident in HBM:
     GEMM  out = sum_kb sX[m,kb] sW[n/128,kb] (X_kb @ W_kb^T), bf16 out
     dequantize X (the activation round trip, codes -> bf16)
 on the DeepSeek-V3-style block-scaled workload M=4096, N=7168, K=7168.
-`value` is 2*M*N*K / (time per step) in TFLOP/s.  The dominant kernel (the
-GEMM) is also timed on its own with HIP events on the launch stream, and
-reported against the fp8 matrix-core peak; the two quantize kernels are
-reported in algorithmic GB/s against the HBM peak.
+`value` is 2*M*N*K / (time per step) in TFLOP/s.  Each kernel is also timed
+on its own (K back-to-back launches between HIP events on the launch stream):
+the dominant kernel (the GEMM) against its matrix-core peak (bf16 for the
+exact default, fp8 for --accum native) or, for the decode workload, against
+the HBM peak; the quantize and dequantize kernels in algorithmic GB/s against
+the HBM peak.
 
 Input sets are rotated (R copies, over 1 GB in total) so that no launch
 reads data another launch left in the 256 MB last-level cache.
@@ -296,54 +298,80 @@ def main(argv=None) -> int:
             fb.fp8_quantize(w, wl.w_fmt, wl.w_gran, q=wq, scales=sw, workspace=wsw, stream=stream)
         torch.cuda.synchronize()
 
-    def step(i, ev=None):
+    def step(i):
         x, w, xq, wq, sx, sw, out, xr = sets[i % R]
-        if ev is not None:
-            ev[0].record(stream)
         fb.fp8_quantize(x, wl.x_fmt, wl.x_gran, q=xq, scales=sx, workspace=wsx, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
         if w_in_step:
             fb.fp8_quantize(w, wl.w_fmt, wl.w_gran, q=wq, scales=sw, workspace=wsw, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
         fb.fp8_gemm_blockscaled(xq, wl.x_fmt, wl.x_gran, sx, wq, wl.w_fmt, wl.w_gran, sw, wl.out_dtype,
                                 out=out, accum=accum, stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
         fb.fp8_dequantize(xq, sx, wl.x_fmt, wl.x_gran, wl.in_dtype, y=xr, stream=stream)
-        if ev is not None:
-            ev[4].record(stream)
 
+    cpu0 = time.perf_counter()
     for i in range(args.warmup):
         step(i)
+    cpu_per_step = (time.perf_counter() - cpu0) / max(1, args.warmup)
     torch.cuda.synchronize()
 
-    # timed region: whole steps, bracketed by synchronizations
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
-    qx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    qw_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    gm_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    dq_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
+    # Small steps take less GPU time than Python takes to enqueue them; the
+    # GPU would then idle between kernels and the events would time the host.
+    # A spin kernel ahead of each timed region keeps the GPU busy until every
+    # timed step is queued, so the region sees back-to-back GPU work only.
+    for _ in range(2):   # the second measurement is warm
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.cuda._sleep(2_000_000)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    cycles_per_ms = 2_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    prefill_ms = min(2000.0, max(5.0, 3.0 * args.steps * cpu_per_step * 1e3))
+
+    def timed():
+        """K steps between two synchronizations; returns (ms per step, wall s)."""
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        torch.cuda._sleep(int(prefill_ms * cycles_per_ms))
+        t_start.record(stream)
+        for i in range(args.steps):
+            step(args.warmup + i)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / args.steps, time.perf_counter() - wall0
+
+    def kernel_ms(launch):
+        """Mean duration of one kernel: K back-to-back launches (rotating over
+        the input sets) between two events on the launch stream."""
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(prefill_ms * cycles_per_ms))
+        t0.record(stream)
+        for i in range(args.steps):
+            launch(sets[(args.warmup + i) % R])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    # The step time (the timed region proper), then each kernel on its own.
+    ms_step, wall = timed()
+    qx_ms = kernel_ms(lambda st: fb.fp8_quantize(st[0], wl.x_fmt, wl.x_gran, q=st[2], scales=st[4], workspace=wsx,
+                                                 stream=stream))
+    qw_ms = kernel_ms(lambda st: fb.fp8_quantize(st[1], wl.w_fmt, wl.w_gran, q=st[3], scales=st[5], workspace=wsw,
+                                                 stream=stream))
+    gm_ms = kernel_ms(lambda st: fb.fp8_gemm_blockscaled(st[2], wl.x_fmt, wl.x_gran, st[4], st[3], wl.w_fmt,
+                                                         wl.w_gran, st[5], wl.out_dtype, out=st[6], accum=accum,
+                                                         stream=stream))
+    dq_ms = kernel_ms(lambda st: fb.fp8_dequantize(st[2], st[4], wl.x_fmt, wl.x_gran, wl.in_dtype, y=st[7],
+                                                   stream=stream))
     dq_gbs = dequant_bytes(wl) / (dq_ms * 1e-3) / 1e9
 
     flops = 2.0 * M * N * K
     value = flops / (ms_step * 1e-3) / 1e12
     gemm_tflops = flops / (gm_ms * 1e-3) / 1e12
     qx_gbs = quant_bytes(wl, "x") / (qx_ms * 1e-3) / 1e9
-    qw_gbs = quant_bytes(wl, "w") / (qw_ms * 1e-3) / 1e9 if w_in_step else None
+    qw_gbs = quant_bytes(wl, "w") / (qw_ms * 1e-3) / 1e9
     gemm_hbm_gbs = gemm_bytes(wl) / (gm_ms * 1e-3) / 1e9
 
     skinny = wl.M <= 32
@@ -386,13 +414,14 @@ def main(argv=None) -> int:
             "gemm_algorithmic_gbs": round(gemm_hbm_gbs, 1),
             "quantize_x_ms": round(qx_ms, 4), "quantize_x_gbs": round(qx_gbs, 1),
             "quantize_x_frac_hbm": round(qx_gbs / PEAK_HBM_GBS, 4),
-            "quantize_w_ms": round(qw_ms, 4) if w_in_step else None,
-            "quantize_w_gbs": round(qw_gbs, 1) if w_in_step else None,
-            "quantize_w_frac_hbm": round(qw_gbs / PEAK_HBM_GBS, 4) if w_in_step else None,
+            "quantize_w_ms": round(qw_ms, 4), "quantize_w_gbs": round(qw_gbs, 1),
+            "quantize_w_frac_hbm": round(qw_gbs / PEAK_HBM_GBS, 4),
+            "quantize_w_in_step": w_in_step,
             "dequantize_x_ms": round(dq_ms, 4), "dequantize_x_gbs": round(dq_gbs, 1),
             "dequantize_x_frac_hbm": round(dq_gbs / PEAK_HBM_GBS, 4),
         },
         "wall_s_timed": round(wall, 4),
+        "queue_prefill_ms": round(prefill_ms, 2),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_sample_rows, M))

@@ -47,13 +47,13 @@ struct SkinnyStage {
 
 // R (W rows per workgroup) <= 16 * T <= 112, so a workgroup's rows touch at
 // most two 128-row W scale blocks and their MX scale words fit two 64-lane loads.
-template <int AF, int BF, int MODE, int ODT, int PATH, int MT, int T, int S>
+template <int AF, int BF, int MODE, int ODT, int PATH, int MT, int T, int S, int NS>
 __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
   static_assert(16 * T <= 112, "a workgroup's rows must touch at most two 128-row scale blocks");
   using St = SkinnyStage<MODE, MT, T>;
-  static_assert(2 * St::kLoads <= 63, "loads in flight must fit the vmcnt counter");
-  static_assert(MT * T * 64 * 16 <= 2 * St::kBytes, "partial tiles must fit in the wave's stages");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[S][2][St::kBytes];
+  static_assert(NS * St::kLoads <= 63, "loads in flight must fit the vmcnt counter");
+  static_assert(MT * T * 64 * 16 <= NS * St::kBytes, "partial tiles must fit in the wave's stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[S][NS][St::kBytes];
 
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t n0 = (int64_t)blockIdx.x * R;
@@ -227,17 +227,20 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
     }
   };
 
-  // Two stages per wave (private: no workgroup barrier in the loop).  The
-  // loads of step k+1 are issued before step k is computed; the explicit wait
-  // leaves exactly those kLoads loads in flight.  Steps past the wave's range
-  // load zeros and are not computed, so every iteration issues the same
-  // number of loads.
+  // NS stages per wave (private: no workgroup barrier in the loop).  The
+  // loads of steps k+1 .. k+NS-1 are in flight while step k is computed; the
+  // explicit wait leaves exactly those loads outstanding.  Steps past the
+  // wave's range load zeros and are not computed, so every iteration issues
+  // the same number of loads.
   if (kb0 < kb1) {
-    issue(kb0, 0);
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) issue(kb0 + j, j);
+    int cs = 0;  // stage of step k
     for (int k = kb0; k < kb1; ++k) {
-      issue(k + 1, (k + 1 - kb0) & 1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(St::kLoads) : "memory");
-      compute((k - kb0) & 1);
+      issue(k + NS - 1, cs == 0 ? NS - 1 : cs - 1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 1) * St::kLoads) : "memory");
+      compute(cs);
+      cs = cs + 1 == NS ? 0 : cs + 1;
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last (zero) loads have landed
@@ -274,7 +277,7 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
 // undefined).
 template <int AF, int BF, int MODE, int ODT, int PATH, int MT, int T>
 __global__ __launch_bounds__(256) void k_gemm_skinny(GemmArgs p, int R) {
-  gemm_skinny_body<AF, BF, MODE, ODT, PATH, MT, T, 4>(p, R);
+  gemm_skinny_body<AF, BF, MODE, ODT, PATH, MT, T, 4, 2>(p, R);  // 3 stages measured no faster
 }
 
 // ---- dispatch ----------------------------------------------------------------

@@ -116,6 +116,23 @@ def test_gemm_skinny_matches_tiled():
         assert np.all(np.abs(a.astype(np.float64) - b) <= 2 * rel * absb)
 
 
+@pytest.mark.parametrize("xg,wg", PAIRS)
+def test_gemm_skinny_partial_tiles(xg, wg):
+    """The skinny kernel gives each workgroup R = ceil(N / grid) rows of W, so a
+    16-column tile is often only partly inside a workgroup's range and a
+    range may straddle a 128-row W scale block: every column must still come
+    out right (M = 16, 48 and 64 use 5, 3 and 2 tiles per workgroup; N = 20608
+    needs two workgroups per compute unit)."""
+    for (M, N, K) in [(16, 4480, 512), (48, 4480, 384), (64, 4480, 256), (16, 20608, 256)]:
+        xq, sx, wq, sw = _operands(M, N, K, xg, wg, fb.E4M3, fb.E5M2, seed=N + M)
+        ref, absb = gemm.gemm_ref(xq, sx, xg, fb.E4M3, wq, sw, wg, fb.E5M2)
+        for accum, rel in ACCUMS:
+            label = f"skinny partial tiles pair=({xg},{wg}) {M}x{N}x{K} accum={accum}"
+            say("gemm", label)
+            out = _run(xq, sx, xg, fb.E4M3, wq, sw, wg, fb.E5M2, fb.DT_F32, fb.GEMM_SKINNY, accum)
+            gemm_check(out, fb.DT_F32, ref, absb, label, rel)
+
+
 def test_gemm_k_zero_writes_zeros():
     say("gemm K=0")
     a = torch.empty((32, 0), dtype=torch.uint8, device="cuda")
