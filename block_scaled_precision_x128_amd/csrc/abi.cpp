@@ -149,6 +149,7 @@ fp8_status_t fp8_gemm_blockscaled_ex(const uint8_t* a, fp8_format_t a_fmt, fp8_g
   p.M = M;
   p.N = N;
   p.K = K;
+  p.ldo = N;
   p.a_per_row = (a_g == FP8_GRAN_ROW);
   p.b_per_row = (b_g == FP8_GRAN_ROW);
   const int path = accum == FP8_ACCUM_NATIVE ? PATH_FAST : PATH_EXACT;

@@ -81,9 +81,10 @@ __device__ __forceinline__ void tile_coords(int64_t bid, int64_t ntm, int64_t nt
 
 
 
-template <int AF, int BF, int MODE, int ODT, int PATH, int WMW, int WNW>
+template <int AF, int BF, int MODE, int ODT, int PATH, int WMW, int WNW, int NJ>
 __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
-  constexpr int TBM = 128 * WMW, TBN = 64 * WNW;       // workgroup tile
+  constexpr int WC = 16 * NJ;                          // columns of a wave tile (NJ 16-column tiles)
+  constexpr int TBM = 128 * WMW, TBN = WC * WNW;       // workgroup tile
   constexpr int NW = WMW * WNW;                        // waves
   constexpr int LPW = (TBM + TBN) / 8 / NW;            // 1-KiB loads per wave per K step
   static_assert((TBM + TBN) % (8 * NW) == 0, "rows must split evenly over the waves");
@@ -98,7 +99,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   tile_coords(blockIdx.x, ntm, ntn, tm, tn);
   const int64_t m0 = tm * TBM, n0 = tn * TBN;
   const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = w / WNW, wn = w % WNW;  // wave tile: rows wm*128.., cols wn*64..
+  const int wm = w / WNW, wn = w % WNW;  // wave tile: rows wm*128.., cols wn*WC..
   const int nkb = (int)(K / 128);
   const int64_t rows_a = (M - m0) < TBM ? (M - m0) : TBM;
   const int64_t rows_b = (N - n0) < TBN ? (N - n0) : TBN;
@@ -170,17 +171,26 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   const int c0 = ((PATH == PATH_EXACT ? 2 * g : g) ^ sw_) << 4;
   const int c1 = ((PATH == PATH_EXACT ? 2 * g + 1 : 4 + g) ^ sw_) << 4;
   const int a_row0 = wm * 128 + (lane & 15);       // + 16 i
-  const int b_row0 = wn * 64 + (lane & 15);        // + 16 j
-  // column block of this wave's 64 columns (for 128x128 weight blocks); a wave
+  const int b_row0 = wn * WC + (lane & 15);        // + 16 j
+  // column block of this wave's columns (for 128x128 weight blocks); a wave
   // whose columns all lie past N (ragged last tile) reads the last block
-  const int64_t nblk_raw = (n0 + wn * 64) / 128, nblk_max = (N + 127) / 128 - 1;
+  const int64_t nblk_raw = (n0 + wn * WC) / 128, nblk_max = (N + 127) / 128 - 1;
   const int64_t nblk = nblk_raw < nblk_max ? nblk_raw : nblk_max;
+  // When a wave's columns can straddle a 128-column block (WC does not divide
+  // 128), each lane takes the W block scale of its own column, per N tile.
+  constexpr bool kWaveWScale = (128 % WC) == 0;
+  int jblk[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int64_t b = (n0 + wn * WC + 16 * j + (lane & 15)) / 128;
+    jblk[j] = (int)((b < nblk_max ? b : nblk_max) - (n0 / 128));
+  }
 
-  v4f acc[8][4];
+  v4f acc[8][NJ];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   if (nkb > 0) issue_loads(0, 0);
 
@@ -194,14 +204,21 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
     const uint8_t* sb_ = &smem[buf][TBM * TBK];
     auto lds16 = [&](const uint8_t* base, int off) { return *reinterpret_cast<const u32x4*>(base + off); };
 
-    float swv = 1.0f;
-    if constexpr (MODE == MODE_PROMOTE) swv = s_w[buf][nblk - wblk0];
+    float swv = 1.0f, swj[NJ];
+    if constexpr (MODE == MODE_PROMOTE) {
+      if constexpr (kWaveWScale) {
+        swv = s_w[buf][nblk - wblk0];
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) swj[j] = s_w[buf][jblk[j]];
+      }
+    }
 
     if constexpr (PATH == PATH_FAST) {
-      v8i fb[4];
-      int eb[4] = {0, 0, 0, 0};
+      v8i fb[NJ];
+      int eb[NJ] = {};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const int r = b_row0 + 16 * j;
         fb[j] = join(lds16(sb_, r * 128 + c0), lds16(sb_, r * 128 + c1));
         if constexpr (MODE == MODE_MX) eb[j] = (int)((s_e[buf][TBM + r] >> (8 * g)) & 0xffu);
@@ -212,28 +229,28 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         const v8i fa = join(lds16(sa_, r * 128 + c0), lds16(sa_, r * 128 + c1));
         if constexpr (MODE == MODE_PROMOTE) {
           const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * 128 + 16 * i + 4 * g]);
-          const v4f sc = {sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};
+          const v4f sc = {sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};  // swv = 1 when per lane
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < NJ; ++j) {
             const v4f pr = mfma_fp8<AF, BF>(fa, fb[j], v4f{0.0f, 0.0f, 0.0f, 0.0f}, (int)kUnitScale, (int)kUnitScale);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(pr[q], sc[q], acc[i][j][q]);
+            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(pr[q], kWaveWScale ? sc[q] : sc[q] * swj[j], acc[i][j][q]);
           }
         } else if constexpr (MODE == MODE_MX) {
           const int ea = (int)((s_e[buf][r] >> (8 * g)) & 0xffu);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp8<AF, BF>(fa, fb[j], acc[i][j], ea, eb[j]);
+          for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_fp8<AF, BF>(fa, fb[j], acc[i][j], ea, eb[j]);
         } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < NJ; ++j)
             acc[i][j] = mfma_fp8<AF, BF>(fa, fb[j], acc[i][j], (int)kUnitScale, (int)kUnitScale);
         }
       }
     } else {
       // Exact path: four K=32 sub-steps on bf16 operands (MX scales folded in).
-      v8bf xb[4][4];
+      v8bf xb[NJ][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const int r = b_row0 + 16 * j;
         const float fsb = (MODE == MODE_MX) ? e8m0_to_f32((s_e[buf][TBM + r] >> (8 * g)) & 0xffu) : 1.0f;
         const u32x4 d0 = lds16(sb_, r * 128 + c0), d1 = lds16(sb_, r * 128 + c1);
@@ -261,24 +278,24 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
             n1 = lds16(sa_, r * 128 + c1);
           }
           const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * 128 + 16 * i + 4 * g]);
-          const v4f sc = {sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};
+          const v4f sc = {sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};  // swv = 1 when per lane
           // Four independent chains (one per N tile), interleaved so that
           // no MFMA waits on the previous one; the wave's priority is raised
           // while it issues them so that a co-resident wave's VALU work fills
           // the gaps instead of delaying the matrix cores.
           __builtin_amdgcn_s_setprio(1);
-          v4f pp[4];
+          v4f pp[NJ];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) pp[j] = mfma_bf16(xa[0], xb[j][0], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+          for (int j = 0; j < NJ; ++j) pp[j] = mfma_bf16(xa[0], xb[j][0], v4f{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
           for (int s = 1; s < 4; ++s)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) pp[j] = mfma_bf16(xa[s], xb[j][s], pp[j]);
+            for (int j = 0; j < NJ; ++j) pp[j] = mfma_bf16(xa[s], xb[j][s], pp[j]);
           __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < NJ; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(pp[j][q], sc[q], acc[i][j][q]);
+            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(pp[j][q], kWaveWScale ? sc[q] : sc[q] * swj[j], acc[i][j][q]);
           if (i + 1 < 8) {
             xa[0] = cvt8<AF>(n0.x, n0.y, 1.0f);
             xa[1] = cvt8<AF>(n0.z, n0.w, 1.0f);
@@ -290,7 +307,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
           // (promotion FMAs and the next tile's conversions).
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-          for (int z = 0; z < 16; ++z) {
+          for (int z = 0; z < 4 * NJ; ++z) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
           }
@@ -309,7 +326,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
 #pragma unroll
           for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(xa[s], xb[j][s], acc[i][j]);
+            for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_bf16(xa[s], xb[j][s], acc[i][j]);
         }
       }
     }
@@ -321,8 +338,8 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
     const int64_t rbase = m0 + wm * 128 + i * 16;
     if (rbase >= M) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t cbase = n0 + wn * 64 + j * 16;
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t cbase = n0 + wn * WC + j * 16;
       if (cbase >= N) continue;
       const int64_t col = cbase + (lane & 15);
       float sbv = 1.0f;
@@ -332,20 +349,25 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         const int64_t row = rbase + 4 * g + q;
         float v = acc[i][j][q];
         if constexpr (MODE == MODE_EPILOGUE) v = v * (sxa[p.a_per_row ? row : 0] * sbv);
-        store_out<ODT>(p.out, row * N + col, v);
+        store_out<ODT>(p.out, row * p.ldo + col, v);
       }
     }
   }
 }
 
-// Kernels for the two workgroup shapes (256x256 with 8 waves, 128x256 with 4).
+// Kernels for the workgroup shapes (256x256 and 256x192 with 8 waves, 128x256
+// with 4).
 template <int AF, int BF, int MODE, int ODT, int PATH>
 __global__ __launch_bounds__(512, 1) void k_gemm_tiled_256x256(GemmArgs p) {
-  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4>(p);
+  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 4>(p);
+}
+template <int AF, int BF, int MODE, int ODT, int PATH>
+__global__ __launch_bounds__(512, 1) void k_gemm_tiled_256x192(GemmArgs p) {
+  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 3>(p);
 }
 template <int AF, int BF, int MODE, int ODT, int PATH>
 __global__ __launch_bounds__(256, 1) void k_gemm_tiled_128x256(GemmArgs p) {
-  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 1, 4>(p);
+  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 1, 4, 4>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -363,18 +385,51 @@ hipError_t launch_fill_zero(void* out, int64_t bytes, hipStream_t st) {
 }
 
 // ---- dispatch over formats, modes, output dtype, path and tile shape ---------
-// Tile shapes: 256x256 (8 waves) when that gives at least one tile per CU,
-// else 128x256 (4 waves).
+// Tile shapes: 256x256 (8 waves) when that gives at least one tile per CU
+// (with a 256x192 remainder, below), else 128x256 (4 waves).
+
+// The columns [c0, c0 + n) of the problem as a problem of its own (c0 is a
+// multiple of 128, so every scale layout splits at a block boundary).
+static GemmArgs column_range(const GemmArgs& p, int64_t c0, int64_t n, int mode, int odt) {
+  GemmArgs q = p;
+  q.b = p.b + c0 * p.K;
+  q.N = n;
+  q.out = static_cast<uint8_t*>(p.out) + c0 * (odt == DT_F32 ? 4 : 2);
+  if (mode == MODE_PROMOTE) q.sb = static_cast<const float*>(p.sb) + (c0 / 128) * (p.K / 128);
+  else if (mode == MODE_MX) q.sb = static_cast<const uint8_t*>(p.sb) + c0 * (p.K / 32);
+  else if (p.b_per_row) q.sb = static_cast<const float*>(p.sb) + c0;
+  return q;
+}
 
 template <int AF, int BF, int MODE, int ODT, int PATH>
 static void tiled_shape(const GemmArgs& p, hipStream_t st) {
-  const int64_t big_tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  if (big_tiles >= num_cus()) {
-    hipLaunchKernelGGL((k_gemm_tiled_256x256<AF, BF, MODE, ODT, PATH>), dim3((unsigned)big_tiles), dim3(512), 0, st, p);
-  } else {
+  const int64_t cus = num_cus();
+  const int64_t ntm = (p.M + 255) / 256;
+  const int64_t big_tiles = ntm * ((p.N + 255) / 256);
+  if (big_tiles < cus) {
     const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 255) / 256);
     hipLaunchKernelGGL((k_gemm_tiled_128x256<AF, BF, MODE, ODT, PATH>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+    return;
   }
+  // A tile count that is not a multiple of the CU count leaves part of the
+  // last wave of workgroups idle.  When the tile rows divide the CUs, the
+  // first N1 columns are done in whole waves of 256x256 tiles and the rest in
+  // one wave of 256x192 tiles (three quarters of the work per tile), launched
+  // right after: e.g. 4096x7168 runs as 256 + 256 tiles in 1.75 tile-times
+  // instead of 448 tiles in 2.
+  if (big_tiles % cus != 0 && cus % ntm == 0) {
+    const int64_t wave_cols = (cus / ntm) * 256;
+    const int64_t n1 = (p.N / wave_cols) * wave_cols, n2 = p.N - n1;
+    if (n1 > 0 && n2 > 0 && ntm * ((n2 + 191) / 192) <= cus) {
+      const GemmArgs p1 = column_range(p, 0, n1, MODE, ODT), p2 = column_range(p, n1, n2, MODE, ODT);
+      hipLaunchKernelGGL((k_gemm_tiled_256x256<AF, BF, MODE, ODT, PATH>), dim3((unsigned)(ntm * (n1 / 256))),
+                         dim3(512), 0, st, p1);
+      hipLaunchKernelGGL((k_gemm_tiled_256x192<AF, BF, MODE, ODT, PATH>), dim3((unsigned)(ntm * ((n2 + 191) / 192))),
+                         dim3(512), 0, st, p2);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_gemm_tiled_256x256<AF, BF, MODE, ODT, PATH>), dim3((unsigned)big_tiles), dim3(512), 0, st, p);
 }
 
 template <int AF, int BF, int MODE, int ODT>

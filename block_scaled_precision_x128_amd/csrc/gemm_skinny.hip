@@ -268,7 +268,7 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
       for (int s = 0; s < S; ++s) v += reinterpret_cast<const float*>(&lds[s][0][0])[(u * 64 + lane) * 4 + r];
       if (row >= M) continue;
       if constexpr (MODE == MODE_EPILOGUE) v = v * (sxa[p.a_per_row ? row : 0] * swb[p.b_per_row ? col : 0]);
-      store_out<ODT>(p.out, row * N + col, v);
+      store_out<ODT>(p.out, row * p.ldo + col, v);
     }
   }
 }

@@ -23,6 +23,7 @@ struct GemmArgs {
   const void* sb;     // scales of b
   void* out;          // [M, N]
   int64_t M, N, K;
+  int64_t ldo;        // elements between consecutive rows of out (>= N)
   int a_per_row;      // epilogue mode: 1 = one scale per row of a, 0 = one per tensor
   int b_per_row;      // epilogue mode: same for b
 };

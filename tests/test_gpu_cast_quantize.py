@@ -92,6 +92,21 @@ def test_quantize_ragged_shapes(gran, fmt, dt):
         _run_quant(x_store, gran, fmt, f"g={gran} f={fmt} dt={dt} {rows}x{cols}")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("dt", [fb.DT_F32, fb.DT_BF16])
+def test_quantize_row_lengths(fmt, dt):
+    """Per-row scales over every row-length class of the row kernels (one
+    workgroup per row holding 2, 4 or 8 chunks of 8 elements per thread, and
+    the two-pass kernel for longer rows)."""
+    wl = workloads.CONFIGS["c2_per_token_channel"]
+    for cols in (2560, 4096, 6272, 8192, 12288, 20480):
+        rows = 5
+        say("quantize row lengths", fmt, dt, rows, cols)
+        x = workloads.draw_x(wl, rows, cols, np.random.default_rng(cols + fmt))
+        x_store = workloads.f32_to_bf16_bits(x) if dt == fb.DT_BF16 else x
+        _run_quant(x_store, fb.GRAN_ROW, fmt, f"row lengths f={fmt} dt={dt} {rows}x{cols}")
+
+
 @pytest.mark.parametrize("gran", GRANS)
 @pytest.mark.parametrize("fmt", FMTS)
 def test_quantize_adversarial_quotients(gran, fmt):

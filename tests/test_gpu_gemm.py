@@ -133,6 +133,28 @@ def test_gemm_skinny_partial_tiles(xg, wg):
             gemm_check(out, fb.DT_F32, ref, absb, label, rel)
 
 
+@pytest.mark.parametrize("xg,wg", [(R, R), (TL, BL), (MX, MX)])
+def test_gemm_tiled_column_split(xg, wg):
+    """M = 4096, N = 4480: 16 x 18 = 288 tiles of 256x256 do not fill whole
+    waves of 256 CUs, so the kernel runs the first 4096 columns as 256x256
+    tiles and the last 384 as 256x192 tiles.  Every column next to the split,
+    the last columns and random positions are checked."""
+    M, N, K = 4096, 4480, 256
+    xq, sx, wq, sw = _operands(M, N, K, xg, wg, fb.E4M3, fb.E4M3, seed=44)
+    rng = np.random.default_rng(45)
+    cols = np.concatenate([np.arange(4032, 4160), np.arange(N - 64, N), rng.integers(0, N, 2048)])
+    mi = np.concatenate([rng.integers(0, M, cols.size)])
+    um, mi_idx = np.unique(mi, return_inverse=True)
+    un, ni_idx = np.unique(cols, return_inverse=True)
+    ref, absb = gemm.gemm_ref_pairs(gemm.dequant_rows(xq[um], sx, xg, fb.E4M3, um),
+                                    gemm.dequant_rows(wq[un], sw, wg, fb.E4M3, un), mi_idx, ni_idx)
+    for accum, rel in ACCUMS:
+        label = f"column split pair=({xg},{wg}) accum={accum}"
+        say("gemm", label)
+        out = _run(xq, sx, xg, fb.E4M3, wq, sw, wg, fb.E4M3, fb.DT_F32, fb.GEMM_TILED, accum)
+        gemm_check(out[mi, cols], fb.DT_F32, ref, absb, label, rel)
+
+
 def test_gemm_k_zero_writes_zeros():
     say("gemm K=0")
     a = torch.empty((32, 0), dtype=torch.uint8, device="cuda")
