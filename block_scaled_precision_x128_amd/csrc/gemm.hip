@@ -44,12 +44,13 @@
 namespace fp8blk {
 
 // ---------------------------------------------------------------------------
-// Tiled kernel: 256x256 output tile per workgroup of 8 waves (2 along M x 4
-// along N, 128x64 each), 128-K steps.  Both operand tiles are FP8 in LDS,
-// double-buffered; global data goes to LDS with buffer_load ... lds (no
-// register staging), through descriptors that cover only the tile's valid
-// rows, so rows past M or N arrive as zeros.  One barrier per K step: the
-// loads of step k+1 are issued right after it and land while step k computes.
+// Tiled kernel: a workgroup of 8 waves (2 along M x 4 along N) computes a
+// 256x256 output tile (wave tiles 128x64; 256x192 and 128x256 variants
+// below), in 128-K steps.  Both operand tiles are FP8 in LDS, in two or three
+// stages; global data goes to LDS with buffer_load ... lds (no register
+// staging), through descriptors that cover only the tile's valid rows, so
+// rows past M or N arrive as zeros.  One barrier per K step: the loads of
+// step k+NS-1 are issued right after it and land while step k computes.
 //
 // LDS tile layout: 128-byte rows of eight 16-byte chunks; chunk c of row r is
 // stored at chunk c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment
@@ -81,17 +82,24 @@ __device__ __forceinline__ void tile_coords(int64_t bid, int64_t ntm, int64_t nt
 
 
 
-template <int AF, int BF, int MODE, int ODT, int PATH, int WMW, int WNW, int NJ>
+template <int AF, int BF, int MODE, int ODT, int PATH, int WMW, int WNW, int MI, int NJ, int NS>
 __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
-  constexpr int WC = 16 * NJ;                          // columns of a wave tile (NJ 16-column tiles)
-  constexpr int TBM = 128 * WMW, TBN = WC * WNW;       // workgroup tile
+  constexpr int WR = 16 * MI, WC = 16 * NJ;            // wave tile: MI x NJ 16x16 output tiles
+  constexpr int TBM = WR * WMW, TBN = WC * WNW;        // workgroup tile
   constexpr int NW = WMW * WNW;                        // waves
   constexpr int LPW = (TBM + TBN) / 8 / NW;            // 1-KiB loads per wave per K step
   static_assert((TBM + TBN) % (8 * NW) == 0, "rows must split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][(TBM + TBN) * TBK];
-  __shared__ __attribute__((aligned(16))) float s_x[2][TBM];                     // MODE_PROMOTE: sA[m, kb]
-  __shared__ __attribute__((aligned(16))) uint32_t s_e[2][TBM + TBN];            // MODE_MX: 4 scale bytes per row
-  __shared__ __attribute__((aligned(16))) float s_w[2][64];                      // MODE_PROMOTE: sB[n/128, kb]
+  constexpr int SCALE_CHUNKS = MODE == MODE_PROMOTE ? TBM / 64 + 1 : (MODE == MODE_MX ? (TBM + TBN) / 64 : 0);
+  constexpr int SC = (SCALE_CHUNKS + NW - 1) / NW;     // scale loads per wave per step
+  constexpr int LOADS = LPW + SC;                      // loads per wave per step
+  static_assert((NS - 1) * LOADS <= 63, "loads in flight must fit the vmcnt counter");
+  static_assert(TBM % 64 == 0 && (TBM + TBN) % 64 == 0, "scale loads move 64 rows at a time");
+  // NS LDS stages; the loads of the next NS-1 K steps are in flight while one is computed.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS][(TBM + TBN) * TBK];
+  __shared__ __attribute__((aligned(16))) float s_x[NS][TBM];                    // MODE_PROMOTE: sA[m, kb]
+  __shared__ __attribute__((aligned(16))) uint32_t s_e[NS][TBM + TBN];           // MODE_MX: 4 scale bytes per row
+  __shared__ __attribute__((aligned(16))) float s_w[NS][64];                     // MODE_PROMOTE: sB[n/128, kb]
+  __shared__ __attribute__((aligned(16))) uint32_t s_spare[64];                  // target of filler loads
 
   const int64_t M = p.M, N = p.N, K = p.K;
   const int64_t ntm = (M + TBM - 1) / TBM, ntn = (N + TBN - 1) / TBN;
@@ -99,7 +107,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   tile_coords(blockIdx.x, ntm, ntn, tm, tn);
   const int64_t m0 = tm * TBM, n0 = tn * TBN;
   const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = w / WNW, wn = w % WNW;  // wave tile: rows wm*128.., cols wn*WC..
+  const int wm = w / WNW, wn = w % WNW;  // wave tile: rows wm*WR.., cols wn*WC..
   const int nkb = (int)(K / 128);
   const int64_t rows_a = (M - m0) < TBM ? (M - m0) : TBM;
   const int64_t rows_b = (N - n0) < TBN ? (N - n0) : TBN;
@@ -146,21 +154,32 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       dma_to_lds<16>(block_rsrc(is_a ? a_base : b_base, is_a ? rows_a : rows_b, is_a ? x : x - TBM / 8),
                      lds_addr(&smem[buf][8 * x * 128]), off);
     }
-    // scales: one 4-byte load per lane, 64 rows per wave; A rows first, then B rows (MX)
+    // Scales, 64 rows per 4-byte load, spread so that every wave issues
+    // exactly SC of them per step (a wave with no chunk left loads zeros into
+    // a spare slot): every wave then issues the same number of loads per
+    // step, which the multi-stage wait below counts on.
     if constexpr (MODE == MODE_PROMOTE) {
-      // the (up to TBN/128 + 1) W block scales of this tile's columns; lanes past them read zeros
-      if (w == NW - 1) dma_to_lds<4>(rssw, lds_addr(&s_w[buf][0]), (lane * nkb + kb) * 4);
 #pragma unroll
-      for (int v = w; v < TBM / 64; v += NW)
-        dma_to_lds<4>(rssa, lds_addr(&s_x[buf][64 * v]), ((64 * v + lane) * nkb + kb) * 4);
+      for (int t2 = 0; t2 < SC; ++t2) {
+        const int c = w + NW * t2;   // chunks 0 .. TBM/64-1: sA rows; chunk TBM/64: the W block scales
+        if (c < TBM / 64)
+          dma_to_lds<4>(rssa, lds_addr(&s_x[buf][64 * c]), ((64 * c + lane) * nkb + kb) * 4);
+        else if (c == TBM / 64)
+          dma_to_lds<4>(rssw, lds_addr(&s_w[buf][0]), (lane * nkb + kb) * 4);
+        else
+          dma_to_lds<4>(rssw, lds_addr(&s_spare[0]), kOutOfRange);
+      }
     }
     if constexpr (MODE == MODE_MX) {
 #pragma unroll
-      for (int v = w; v < (TBM + TBN) / 64; v += NW) {
-        if (v < TBM / 64)
-          dma_to_lds<4>(rssa, lds_addr(&s_e[buf][64 * v]), (int)((64 * v + lane) * kq + kb * 4));
+      for (int t2 = 0; t2 < SC; ++t2) {
+        const int c = w + NW * t2;   // chunks of 64 rows: A rows first, then B rows
+        if (c < TBM / 64)
+          dma_to_lds<4>(rssa, lds_addr(&s_e[buf][64 * c]), (int)((64 * c + lane) * kq + kb * 4));
+        else if (c < (TBM + TBN) / 64)
+          dma_to_lds<4>(rssb, lds_addr(&s_e[buf][64 * c]), (int)((64 * c - TBM + lane) * kq + kb * 4));
         else
-          dma_to_lds<4>(rssb, lds_addr(&s_e[buf][64 * v]), (int)((64 * v - TBM + lane) * kq + kb * 4));
+          dma_to_lds<4>(rssb, lds_addr(&s_spare[0]), kOutOfRange);
       }
     }
   };
@@ -170,7 +189,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   const int g = lane >> 4, sw_ = lds_swz(lane & 15);
   const int c0 = ((PATH == PATH_EXACT ? 2 * g : g) ^ sw_) << 4;
   const int c1 = ((PATH == PATH_EXACT ? 2 * g + 1 : 4 + g) ^ sw_) << 4;
-  const int a_row0 = wm * 128 + (lane & 15);       // + 16 i
+  const int a_row0 = wm * WR + (lane & 15);       // + 16 i
   const int b_row0 = wn * WC + (lane & 15);        // + 16 j
   // column block of this wave's columns (for 128x128 weight blocks); a wave
   // whose columns all lie past N (ragged last tile) reads the last block
@@ -186,19 +205,30 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
     jblk[j] = (int)((b < nblk_max ? b : nblk_max) - (n0 / 128));
   }
 
-  v4f acc[8][NJ];
+  v4f acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (nkb > 0) issue_loads(0, 0);
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < nkb) issue_loads(j, j);
 
+  int buf = 0;   // stage of step kb
   for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Wait for this step's loads; those of later steps stay in flight (every
+    // wave issues LOADS per step, and loads complete in issue order).
+    if constexpr (NS == 3) {
+      if (kb + 1 < nkb) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      static_assert(NS == 2, "two or three stages");
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
-    if (kb + 1 < nkb) issue_loads(kb + 1, buf ^ 1);
+    // The stage read in the previous step is free now: load step kb+NS-1 into it.
+    if (kb + NS - 1 < nkb) issue_loads(kb + NS - 1, buf == 0 ? NS - 1 : buf - 1);
 
     const uint8_t* sa_ = &smem[buf][0];
     const uint8_t* sb_ = &smem[buf][TBM * TBK];
@@ -224,11 +254,11 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         if constexpr (MODE == MODE_MX) eb[j] = (int)((s_e[buf][TBM + r] >> (8 * g)) & 0xffu);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < MI; ++i) {
         const int r = a_row0 + 16 * i;
         const v8i fa = join(lds16(sa_, r * 128 + c0), lds16(sa_, r * 128 + c1));
         if constexpr (MODE == MODE_PROMOTE) {
-          const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * 128 + 16 * i + 4 * g]);
+          const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * WR + 16 * i + 4 * g]);
           const v4f sc = {sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};  // swv = 1 when per lane
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
@@ -271,13 +301,13 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         xa[2] = cvt8<AF>(n1.x, n1.y, 1.0f);
         xa[3] = cvt8<AF>(n1.z, n1.w, 1.0f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (i + 1 < 8) {
+        for (int i = 0; i < MI; ++i) {
+          if (i + 1 < MI) {
             const int r = a_row0 + 16 * (i + 1);
             n0 = lds16(sa_, r * 128 + c0);
             n1 = lds16(sa_, r * 128 + c1);
           }
-          const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * 128 + 16 * i + 4 * g]);
+          const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * WR + 16 * i + 4 * g]);
           const v4f sc = {sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};  // swv = 1 when per lane
           // Four independent chains (one per N tile), interleaved so that
           // no MFMA waits on the previous one; the wave's priority is raised
@@ -296,7 +326,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
           for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(pp[j][q], kWaveWScale ? sc[q] : sc[q] * swj[j], acc[i][j][q]);
-          if (i + 1 < 8) {
+          if (i + 1 < MI) {
             xa[0] = cvt8<AF>(n0.x, n0.y, 1.0f);
             xa[1] = cvt8<AF>(n0.z, n0.w, 1.0f);
             xa[2] = cvt8<AF>(n1.x, n1.y, 1.0f);
@@ -314,7 +344,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < MI; ++i) {
           const int r = a_row0 + 16 * i;
           const float fsa = (MODE == MODE_MX) ? e8m0_to_f32((s_e[buf][r] >> (8 * g)) & 0xffu) : 1.0f;
           const u32x4 d0 = lds16(sa_, r * 128 + c0), d1 = lds16(sa_, r * 128 + c1);
@@ -330,12 +360,13 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         }
       }
     }
+    buf = buf + 1 == NS ? 0 : buf + 1;
   }
 
   // epilogue
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t rbase = m0 + wm * 128 + i * 16;
+  for (int i = 0; i < MI; ++i) {
+    const int64_t rbase = m0 + wm * WR + i * 16;
     if (rbase >= M) continue;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -355,20 +386,24 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   }
 }
 
-// Kernels for the workgroup shapes (256x256 and 256x192 with 8 waves, 128x256
-// with 4).
+// Kernels for the workgroup shapes, all with 8 waves: 256x256 and 256x192
+// (wave tiles 128x64 and 128x48, two LDS stages), and 128x256 (wave tiles
+// 64x64, three LDS stages) for problems with fewer 256x256 tiles than CUs,
+// where the deeper pipeline measured 13% faster and the smaller tile's lower
+// arithmetic intensity does not matter.
 template <int AF, int BF, int MODE, int ODT, int PATH>
 __global__ __launch_bounds__(512, 1) void k_gemm_tiled_256x256(GemmArgs p) {
-  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 4>(p);
+  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 8, 4, 2>(p);
 }
 template <int AF, int BF, int MODE, int ODT, int PATH>
 __global__ __launch_bounds__(512, 1) void k_gemm_tiled_256x192(GemmArgs p) {
-  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 3>(p);
+  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 8, 3, 2>(p);
 }
 template <int AF, int BF, int MODE, int ODT, int PATH>
-__global__ __launch_bounds__(256, 1) void k_gemm_tiled_128x256(GemmArgs p) {
-  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 1, 4, 4>(p);
+__global__ __launch_bounds__(512, 1) void k_gemm_tiled_128x256(GemmArgs p) {
+  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 4, 4, 3>(p);
 }
+
 
 // ---------------------------------------------------------------------------
 __global__ void k_fill_zero(uint32_t* p, int64_t nwords) {
@@ -385,8 +420,8 @@ hipError_t launch_fill_zero(void* out, int64_t bytes, hipStream_t st) {
 }
 
 // ---- dispatch over formats, modes, output dtype, path and tile shape ---------
-// Tile shapes: 256x256 (8 waves) when that gives at least one tile per CU
-// (with a 256x192 remainder, below), else 128x256 (4 waves).
+// Tile shapes: 256x256 when that gives at least one tile per CU (with a
+// 256x192 remainder, below), else 128x256.
 
 // The columns [c0, c0 + n) of the problem as a problem of its own (c0 is a
 // multiple of 128, so every scale layout splits at a block boundary).
@@ -408,7 +443,7 @@ static void tiled_shape(const GemmArgs& p, hipStream_t st) {
   const int64_t big_tiles = ntm * ((p.N + 255) / 256);
   if (big_tiles < cus) {
     const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 255) / 256);
-    hipLaunchKernelGGL((k_gemm_tiled_128x256<AF, BF, MODE, ODT, PATH>), dim3((unsigned)tiles), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((k_gemm_tiled_128x256<AF, BF, MODE, ODT, PATH>), dim3((unsigned)tiles), dim3(512), 0, st, p);
     return;
   }
   // A tile count that is not a multiple of the CU count leaves part of the
