@@ -294,7 +294,7 @@ def main(argv=None) -> int:
     wsw = torch.empty(max(1, fb.fp8_quantize_workspace_bytes(N, K, wl.w_gran)), dtype=torch.uint8, device=dev)
     # Decode: the weights are quantized once (setup), the step quantizes the
     # activations and runs the GEMM.
-    w_in_step = wl.M > 32
+    w_in_step = wl.M > 64
     if not w_in_step:
         for x, w, xq, wq, sx, sw, out, xr in sets:
             fb.fp8_quantize(w, wl.w_fmt, wl.w_gran, q=wq, scales=sw, workspace=wsw, stream=stream)
@@ -376,7 +376,7 @@ def main(argv=None) -> int:
     qw_gbs = quant_bytes(wl, "w") / (qw_ms * 1e-3) / 1e9
     gemm_hbm_gbs = gemm_bytes(wl) / (gm_ms * 1e-3) / 1e9
 
-    skinny = wl.M <= 32
+    skinny = wl.M <= 64
     traffic = read_traffic(wl.name, args.accum)
     # The default accumulation runs on the bf16 matrix cores (exact products of
     # the expanded codes, fp32 sums): its own dtype's dense peak is 2.5 PFLOP/s.

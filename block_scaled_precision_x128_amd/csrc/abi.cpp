@@ -153,7 +153,7 @@ fp8_status_t fp8_gemm_blockscaled_ex(const uint8_t* a, fp8_format_t a_fmt, fp8_g
   p.a_per_row = (a_g == FP8_GRAN_ROW);
   p.b_per_row = (b_g == FP8_GRAN_ROW);
   const int path = accum == FP8_ACCUM_NATIVE ? PATH_FAST : PATH_EXACT;
-  const bool skinny = (algo == FP8_GEMM_SKINNY) || (algo == FP8_GEMM_AUTO && M <= 32);
+  const bool skinny = (algo == FP8_GEMM_SKINNY) || (algo == FP8_GEMM_AUTO && M <= 64);
   if (skinny) return hip_status(launch_gemm_skinny(p, (int)a_fmt, (int)b_fmt, mode, (int)out_dt, path, stream));
   return hip_status(launch_gemm_tiled(p, (int)a_fmt, (int)b_fmt, mode, (int)out_dt, path, stream));
 }

@@ -281,9 +281,11 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(GemmArgs p, int R) {
 }
 
 // ---- dispatch ----------------------------------------------------------------
-// Tiles per workgroup by M (registers stay bounded): M <= 16: up to 5 tiles
-// (R <= 80 rows), M <= 32: 3 (R <= 48), M <= 64: 2 (R <= 32).  The grid is
-// c * CUs workgroups with the smallest c that keeps R within that bound.
+// Up to 5 column tiles per workgroup (R <= 80 rows) for every M: one
+// workgroup per CU up to N = 80 * CUs (the stages of M = 64 take 148 KB of
+// LDS; fewer tiles per workgroup would need several workgroups per CU, each
+// reading all of X, and measured slower).  The grid is c * CUs workgroups with
+// the smallest c that keeps R within that bound.
 template <int AF, int BF, int MODE, int ODT, int PATH, int MT, int T>
 static void skinny_launch(const GemmArgs& p, hipStream_t st) {
   const int64_t cus = num_cus();
@@ -298,8 +300,8 @@ template <int AF, int BF, int MODE, int ODT, int PATH>
 static void skinny_mt(const GemmArgs& p, hipStream_t st) {
   const int64_t mt = (p.M + 15) / 16;
   if (mt <= 1) skinny_launch<AF, BF, MODE, ODT, PATH, 1, 5>(p, st);
-  else if (mt <= 2) skinny_launch<AF, BF, MODE, ODT, PATH, 2, 3>(p, st);
-  else skinny_launch<AF, BF, MODE, ODT, PATH, 4, 2>(p, st);
+  else if (mt <= 2) skinny_launch<AF, BF, MODE, ODT, PATH, 2, 5>(p, st);
+  else skinny_launch<AF, BF, MODE, ODT, PATH, 4, 5>(p, st);
 }
 
 template <int AF, int BF, int MODE, int ODT>

@@ -83,7 +83,7 @@ typedef enum {
 typedef enum { FP8_DT_F32 = 0, FP8_DT_BF16 = 1 } fp8_dtype_t;
 
 /* Kernel choice for the GEMM.  AUTO picks the skinny (weight-streaming) kernel
- * for M <= 32 and the tiled MFMA kernel otherwise. */
+ * for M <= 64 and the tiled MFMA kernel otherwise. */
 typedef enum { FP8_GEMM_AUTO = 0, FP8_GEMM_TILED = 1, FP8_GEMM_SKINNY = 2 } fp8_gemm_algo_t;
 
 /* Accumulation of the FP8 products in the GEMM.
