@@ -367,6 +367,20 @@ def main(argv=None) -> int:
                                                          stream=stream))
     dq_ms = kernel_ms(lambda st: fb.fp8_dequantize(st[2], st[4], wl.x_fmt, wl.x_gran, wl.in_dtype, y=st[7],
                                                    stream=stream))
+    # The next row of the path: the GEMM with its output quantized in the
+    # epilogue (E4M3 codes + 1x128 tile scales), against the GEMM followed by
+    # a separate quantize of its output.
+    fused = None
+    if wl.M > 64 and N % 128 == 0:
+        oq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+        osc = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
+        fq_ms = kernel_ms(lambda st: fb.fp8_gemm_blockscaled_quant(st[2], wl.x_fmt, wl.x_gran, st[4], st[3], wl.w_fmt,
+                                                                   wl.w_gran, st[5], fb.E4M3, codes=oq, scales=osc,
+                                                                   accum=accum, stream=stream))
+        qo_ms = kernel_ms(lambda st: fb.fp8_quantize(st[6], fb.E4M3, fb.GRAN_TILE_1x128, q=oq, scales=osc,
+                                                     stream=stream))
+        fused = {"gemm_quantized_out_ms": round(fq_ms, 4), "gemm_then_quantize_ms": round(gm_ms + qo_ms, 4),
+                 "quantize_out_ms": round(qo_ms, 4)}
     dq_gbs = dequant_bytes(wl) / (dq_ms * 1e-3) / 1e9
 
     flops = 2.0 * M * N * K
@@ -421,6 +435,7 @@ def main(argv=None) -> int:
             "quantize_w_in_step": w_in_step,
             "dequantize_x_ms": round(dq_ms, 4), "dequantize_x_gbs": round(dq_gbs, 1),
             "dequantize_x_frac_hbm": round(dq_gbs / PEAK_HBM_GBS, 4),
+            "fused_epilogue_quantize": fused,
         },
         "wall_s_timed": round(wall, 4),
         "queue_prefill_ms": round(prefill_ms, 2),

@@ -52,6 +52,10 @@ _SIGS = {
                                            _c.c_void_p, _c.c_int, _c.c_int, _c.c_void_p,
                                            _c.c_int64, _c.c_int64, _c.c_int64,
                                            _c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_void_p]),
+    "fp8_gemm_blockscaled_quant": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_void_p,
+                                              _c.c_void_p, _c.c_int, _c.c_int, _c.c_void_p,
+                                              _c.c_int64, _c.c_int64, _c.c_int64,
+                                              _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -199,3 +203,22 @@ def fp8_gemm_blockscaled(a, a_fmt: int, a_gran: int, a_scales, b, b_fmt: int, b_
         M, N, K, out.data_ptr(), out_dtype, algo, accum, _stream(stream))
     _check("fp8_gemm_blockscaled", st)
     return out
+
+
+def fp8_gemm_blockscaled_quant(a, a_fmt: int, a_gran: int, a_scales, b, b_fmt: int, b_gran: int, b_scales,
+                               out_fmt: int = E4M3, codes=None, scales=None, accum: int = ACCUM_FP32, stream=None):
+    """The GEMM with its result quantized in the epilogue to out_fmt codes and
+    1x128 tile scales (the layout fp8_quantize writes for GRAN_TILE_1x128).
+    Returns (codes uint8 [M, N], scales float32 [M, N/128])."""
+    torch = _torch()
+    M, K = a.shape
+    N = b.shape[0]
+    if codes is None:
+        codes = torch.empty((M, N), dtype=torch.uint8, device=a.device)
+    if scales is None:
+        scales = torch.empty((M, N // 128), dtype=torch.float32, device=a.device)
+    st = load_library().fp8_gemm_blockscaled_quant(
+        a.data_ptr(), a_fmt, a_gran, a_scales.data_ptr(), b.data_ptr(), b_fmt, b_gran, b_scales.data_ptr(),
+        M, N, K, out_fmt, codes.data_ptr(), scales.data_ptr(), accum, _stream(stream))
+    _check("fp8_gemm_blockscaled_quant", st)
+    return codes, scales

@@ -106,21 +106,19 @@ fp8_status_t fp8_cast(const void* x, fp8_dtype_t x_dt, int64_t n, fp8_format_t f
   return hip_status(launch_cast(x, (int)x_dt, n, (int)fmt, q, stream));
 }
 
-fp8_status_t fp8_gemm_blockscaled_ex(const uint8_t* a, fp8_format_t a_fmt, fp8_granularity_t a_g,
-                                     const void* a_scales, const uint8_t* b, fp8_format_t b_fmt,
-                                     fp8_granularity_t b_g, const void* b_scales, int64_t M, int64_t N, int64_t K,
-                                     void* out, fp8_dtype_t out_dt, fp8_gemm_algo_t algo, fp8_accum_t accum,
-                                     hipStream_t stream) {
-  if (!valid_fmt(a_fmt) || !valid_fmt(b_fmt) || !valid_gran(a_g) || !valid_gran(b_g) || !valid_dt(out_dt))
-    return FP8_ERR_ENUM;
-  if (algo != FP8_GEMM_AUTO && algo != FP8_GEMM_TILED && algo != FP8_GEMM_SKINNY) return FP8_ERR_ENUM;
+namespace {
+
+// Validation and mode selection shared by the GEMM entry points; fills p
+// (without the output) and the scale mode.  Returns FP8_OK or an error.
+fp8_status_t gemm_common(const uint8_t* a, fp8_format_t a_fmt, fp8_granularity_t a_g, const void* a_scales,
+                         const uint8_t* b, fp8_format_t b_fmt, fp8_granularity_t b_g, const void* b_scales,
+                         int64_t M, int64_t N, int64_t K, fp8_accum_t accum, GemmArgs& p, int& mode) {
+  if (!valid_fmt(a_fmt) || !valid_fmt(b_fmt) || !valid_gran(a_g) || !valid_gran(b_g)) return FP8_ERR_ENUM;
   if (accum != FP8_ACCUM_FP32 && accum != FP8_ACCUM_NATIVE) return FP8_ERR_ENUM;
   if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 128) return FP8_ERR_SHAPE;
   if (K > kMaxGemmK) return FP8_ERR_SHAPE;
   if (mul_checked(M, K) < 0 || mul_checked(N, K) < 0 || mul_checked(M, N) < 0) return FP8_ERR_SHAPE;
   if ((M / 128 + 1) * (N / 128 + 1) >= INT_MAX || N / 16 >= INT_MAX) return FP8_ERR_SHAPE;
-
-  int mode;
   const bool a_tr = (a_g == FP8_GRAN_TENSOR || a_g == FP8_GRAN_ROW);
   const bool b_tr = (b_g == FP8_GRAN_TENSOR || b_g == FP8_GRAN_ROW);
   if (a_tr && b_tr) mode = MODE_EPILOGUE;
@@ -128,6 +126,41 @@ fp8_status_t fp8_gemm_blockscaled_ex(const uint8_t* a, fp8_format_t a_fmt, fp8_g
   else if (a_g == FP8_GRAN_MX32 && b_g == FP8_GRAN_MX32) mode = MODE_MX;
   else return FP8_ERR_UNSUPPORTED;
   if (b_g == FP8_GRAN_BLOCK_128x128 && N % 128) return FP8_ERR_SHAPE;
+  p = GemmArgs{};
+  p.a = a;
+  p.b = b;
+  p.sa = a_scales;
+  p.sb = b_scales;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.ldo = N;
+  p.a_per_row = (a_g == FP8_GRAN_ROW);
+  p.b_per_row = (b_g == FP8_GRAN_ROW);
+  return FP8_OK;
+}
+
+fp8_status_t check_operands(const GemmArgs& p) {
+  if (!p.a || !p.b || !p.sa || !p.sb) return FP8_ERR_NULL;
+  if (!aligned(p.a, 16) || !aligned(p.b, 16)) return FP8_ERR_ALIGN;
+  // fp32 scales are read as floats; UE8M0 scales as 4-byte words (4 blocks of 32)
+  if (!aligned(p.sa, 4) || !aligned(p.sb, 4)) return FP8_ERR_ALIGN;
+  return FP8_OK;
+}
+
+}  // namespace
+
+fp8_status_t fp8_gemm_blockscaled_ex(const uint8_t* a, fp8_format_t a_fmt, fp8_granularity_t a_g,
+                                     const void* a_scales, const uint8_t* b, fp8_format_t b_fmt,
+                                     fp8_granularity_t b_g, const void* b_scales, int64_t M, int64_t N, int64_t K,
+                                     void* out, fp8_dtype_t out_dt, fp8_gemm_algo_t algo, fp8_accum_t accum,
+                                     hipStream_t stream) {
+  if (!valid_dt(out_dt)) return FP8_ERR_ENUM;
+  if (algo != FP8_GEMM_AUTO && algo != FP8_GEMM_TILED && algo != FP8_GEMM_SKINNY) return FP8_ERR_ENUM;
+  GemmArgs p;
+  int mode = 0;
+  const fp8_status_t st = gemm_common(a, a_fmt, a_g, a_scales, b, b_fmt, b_g, b_scales, M, N, K, accum, p, mode);
+  if (st != FP8_OK) return st;
   if (algo == FP8_GEMM_SKINNY && M > 64) return FP8_ERR_UNSUPPORTED;
 
   if (M == 0 || N == 0) return FP8_OK;
@@ -135,27 +168,42 @@ fp8_status_t fp8_gemm_blockscaled_ex(const uint8_t* a, fp8_format_t a_fmt, fp8_g
   if (!aligned(out, 16)) return FP8_ERR_ALIGN;
   const int64_t out_bytes = M * N * (out_dt == FP8_DT_F32 ? 4 : 2);
   if (K == 0) return hip_status(launch_fill_zero(out, out_bytes, stream));
-  if (!a || !b || !a_scales || !b_scales) return FP8_ERR_NULL;
-  if (!aligned(a, 16) || !aligned(b, 16)) return FP8_ERR_ALIGN;
-  // fp32 scales are read as floats; UE8M0 scales as 4-byte words (4 blocks of 32)
-  if (!aligned(a_scales, 4) || !aligned(b_scales, 4)) return FP8_ERR_ALIGN;
-
-  GemmArgs p;
-  p.a = a;
-  p.b = b;
-  p.sa = a_scales;
-  p.sb = b_scales;
+  const fp8_status_t so = check_operands(p);
+  if (so != FP8_OK) return so;
   p.out = out;
-  p.M = M;
-  p.N = N;
-  p.K = K;
-  p.ldo = N;
-  p.a_per_row = (a_g == FP8_GRAN_ROW);
-  p.b_per_row = (b_g == FP8_GRAN_ROW);
   const int path = accum == FP8_ACCUM_NATIVE ? PATH_FAST : PATH_EXACT;
   const bool skinny = (algo == FP8_GEMM_SKINNY) || (algo == FP8_GEMM_AUTO && M <= 64);
   if (skinny) return hip_status(launch_gemm_skinny(p, (int)a_fmt, (int)b_fmt, mode, (int)out_dt, path, stream));
   return hip_status(launch_gemm_tiled(p, (int)a_fmt, (int)b_fmt, mode, (int)out_dt, path, stream));
+}
+
+fp8_status_t fp8_gemm_blockscaled_quant(const uint8_t* a, fp8_format_t a_fmt, fp8_granularity_t a_g,
+                                        const void* a_scales, const uint8_t* b, fp8_format_t b_fmt,
+                                        fp8_granularity_t b_g, const void* b_scales, int64_t M, int64_t N,
+                                        int64_t K, fp8_format_t out_fmt, uint8_t* out_codes, float* out_scales,
+                                        fp8_accum_t accum, hipStream_t stream) {
+  if (!valid_fmt(out_fmt)) return FP8_ERR_ENUM;
+  GemmArgs p;
+  int mode = 0;
+  const fp8_status_t st = gemm_common(a, a_fmt, a_g, a_scales, b, b_fmt, b_g, b_scales, M, N, K, accum, p, mode);
+  if (st != FP8_OK) return st;
+  if (N % 128) return FP8_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8_OK;
+  if (!out_codes || !out_scales) return FP8_ERR_NULL;
+  if (!aligned(out_codes, 16) || !aligned(out_scales, 4)) return FP8_ERR_ALIGN;
+  const int odt = out_fmt == FP8_E4M3 ? ODT_Q_E4M3 : ODT_Q_E5M2;
+  p.out = out_codes;
+  p.out_scales = out_scales;
+  if (K == 0) {
+    // all-zero result: codes 0, and the scale of an all-zero tile is 1
+    const hipError_t e = launch_fill_zero(out_codes, M * N, stream);
+    if (e != hipSuccess) return FP8_ERR_HIP;
+    return hip_status(launch_fill_f32(out_scales, M * (N / 128), 1.0f, stream));
+  }
+  const fp8_status_t so = check_operands(p);
+  if (so != FP8_OK) return so;
+  const int path = accum == FP8_ACCUM_NATIVE ? PATH_FAST : PATH_EXACT;
+  return hip_status(launch_gemm_tiled(p, (int)a_fmt, (int)b_fmt, mode, odt, path, stream));
 }
 
 fp8_status_t fp8_gemm_blockscaled(const uint8_t* a, fp8_format_t a_fmt, fp8_granularity_t a_g,

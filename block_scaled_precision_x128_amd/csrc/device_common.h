@@ -105,6 +105,35 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   return e;
 }
 
+template <int N>
+__device__ __forceinline__ float local_amax(const float* v) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) m = fmaxf(m, fabsf(v[i]));
+  return m;
+}
+
+// Encode N (multiple of 4) values with the fp32 scale s into N/4 packed words.
+template <int FMT, int N>
+__device__ __forceinline__ void encode_scaled(const float* v, float s, uint32_t* out) {
+  if (__builtin_expect(s >= 0x1p-64f, 1)) {
+    const float y = 1.0f / s;
+#pragma unroll
+    for (int j = 0; j < N / 4; ++j)
+      out[j] = encode4<FMT>(div_by_scale(v[4 * j], s, y), div_by_scale(v[4 * j + 1], s, y),
+                            div_by_scale(v[4 * j + 2], s, y), div_by_scale(v[4 * j + 3], s, y));
+  } else {
+    // Tiny scale: scale x and s by 2^64 (exact) so that the quotient's
+    // Newton steps stay in the normal range; the quotient is unchanged.
+    const float s2 = s * 0x1p64f;
+    const float y = 1.0f / s2;
+#pragma unroll
+    for (int j = 0; j < N / 4; ++j)
+      out[j] = encode4<FMT>(div_by_scale(v[4 * j] * 0x1p64f, s2, y), div_by_scale(v[4 * j + 1] * 0x1p64f, s2, y),
+                            div_by_scale(v[4 * j + 2] * 0x1p64f, s2, y), div_by_scale(v[4 * j + 3] * 0x1p64f, s2, y));
+  }
+}
+
 // ---- cross-lane max (values are >= 0) --------------------------------------
 // DPP row controls: quad_perm [1,0,3,2] (0xB1), [2,3,0,1] (0x4E),
 // row_half_mirror (0x141), row_mirror (0x140).

@@ -364,23 +364,83 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   }
 
   // epilogue
+  if constexpr (ODT == ODT_Q_E4M3 || ODT == ODT_Q_E5M2) {
+    // The result quantized to FP8 for the next layer, exactly as the
+    // quantizer does it to the fp32 values the DT_F32 output would hold:
+    // per row and 128 columns, amax -> s = RN(amax / Vmax) -> sat_rne(RN(v / s)).
+    // A 128-column group is the tiles of two neighbouring waves (wn, wn ^ 1).
+    constexpr int QF = ODT == ODT_Q_E4M3 ? FMT_E4M3 : FMT_E5M2;
+    static_assert(WC == 64 && WNW % 2 == 0, "a 128-column group must be two 64-column wave tiles");
+    __shared__ float s_amax[NW][WR];
+    if constexpr (MODE == MODE_EPILOGUE) {
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int64_t rbase = m0 + wm * WR + i * 16;
-    if (rbase >= M) continue;
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int64_t cbase = n0 + wn * WC + j * 16;
-      if (cbase >= N) continue;
-      const int64_t col = cbase + (lane & 15);
-      float sbv = 1.0f;
-      if constexpr (MODE == MODE_EPILOGUE) sbv = swb[p.b_per_row ? col : 0];
+        for (int j = 0; j < NJ; ++j) {
+          int64_t col = n0 + wn * WC + j * 16 + (lane & 15);
+          col = col < N ? col : N - 1;   // columns past N hold zeros and are not stored
+          const float sbv = swb[p.b_per_row ? col : 0];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            int64_t row = m0 + wm * WR + i * 16 + 4 * g + q;
+            row = row < M ? row : M - 1;   // rows past M are not stored
+            acc[i][j][q] = acc[i][j][q] * (sxa[p.a_per_row ? row : 0] * sbv);
+          }
+        }
+    }
+    float rmax[MI][4];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) m = fmaxf(m, fabsf(acc[i][j][q]));
+        rmax[i][q] = group_max<16>(m);   // over the 16 lanes that hold this row
+        if ((lane & 15) == 0) s_amax[w][16 * i + 4 * g + q] = rmax[i][q];
+      }
+    __syncthreads();
+    const int64_t nsg = N / 128;                     // scale groups per row
+    const int64_t grp = (n0 + wn * WC) / 128;        // this wave's group
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int64_t rbase = m0 + wm * WR + i * 16;
+      if (rbase >= M) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t row = rbase + 4 * g + q;
-        float v = acc[i][j][q];
-        if constexpr (MODE == MODE_EPILOGUE) v = v * (sxa[p.a_per_row ? row : 0] * sbv);
-        store_out<ODT>(p.out, row * p.ldo + col, v);
+        const float amax = fmaxf(rmax[i][q], s_amax[w ^ 1][16 * i + 4 * g + q]);
+        const float s = group_scale<QF>(amax);
+        const float v4[4] = {acc[i][0][q], acc[i][1][q], acc[i][2][q], acc[i][3][q]};
+        uint32_t codes;
+        encode_scaled<QF, 4>(v4, s, &codes);
+        if (grp < nsg) {
+          uint8_t* o = static_cast<uint8_t*>(p.out) + row * p.ldo + n0 + wn * WC + (lane & 15);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) o[16 * j] = (uint8_t)(codes >> (8 * j));
+          if ((wn & 1) == 0 && (lane & 15) == 0) p.out_scales[row * nsg + grp] = s;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int64_t rbase = m0 + wm * WR + i * 16;
+      if (rbase >= M) continue;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t cbase = n0 + wn * WC + j * 16;
+        if (cbase >= N) continue;
+        const int64_t col = cbase + (lane & 15);
+        float sbv = 1.0f;
+        if constexpr (MODE == MODE_EPILOGUE) sbv = swb[p.b_per_row ? col : 0];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t row = rbase + 4 * g + q;
+          float v = acc[i][j][q];
+          if constexpr (MODE == MODE_EPILOGUE) v = v * (sxa[p.a_per_row ? row : 0] * sbv);
+          store_out<ODT>(p.out, row * p.ldo + col, v);
+        }
       }
     }
   }
@@ -406,17 +466,23 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled_128x256(GemmArgs p) {
 
 
 // ---------------------------------------------------------------------------
-__global__ void k_fill_zero(uint32_t* p, int64_t nwords) {
+__global__ void k_fill_u32(uint32_t* p, int64_t nwords, uint32_t v) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < nwords) p[i] = 0u;
+  if (i < nwords) p[i] = v;
+}
+
+static hipError_t fill_u32(uint32_t* p, int64_t nwords, uint32_t v, hipStream_t st) {
+  if (nwords == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, st, p, nwords, v);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(void* out, int64_t bytes, hipStream_t st) {
-  const int64_t nwords = bytes / 4;
-  if (nwords == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<uint32_t*>(out), nwords);
-  return hipGetLastError();
+  return fill_u32(reinterpret_cast<uint32_t*>(out), bytes / 4, 0u, st);
+}
+
+hipError_t launch_fill_f32(float* out, int64_t n, float v, hipStream_t st) {
+  return fill_u32(reinterpret_cast<uint32_t*>(out), n, __builtin_bit_cast(uint32_t, v), st);
 }
 
 // ---- dispatch over formats, modes, output dtype, path and tile shape ---------
@@ -452,15 +518,17 @@ static void tiled_shape(const GemmArgs& p, hipStream_t st) {
   // one wave of 256x192 tiles (three quarters of the work per tile), launched
   // right after: e.g. 4096x7168 runs as 256 + 256 tiles in 1.75 tile-times
   // instead of 448 tiles in 2.
-  if (big_tiles % cus != 0 && cus % ntm == 0) {
+  // (The quantized outputs need 64-column wave tiles: no split for them.)
+  if (ODT < ODT_Q_E4M3 && big_tiles % cus != 0 && cus % ntm == 0) {
     const int64_t wave_cols = (cus / ntm) * 256;
     const int64_t n1 = (p.N / wave_cols) * wave_cols, n2 = p.N - n1;
     if (n1 > 0 && n2 > 0 && ntm * ((n2 + 191) / 192) <= cus) {
       const GemmArgs p1 = column_range(p, 0, n1, MODE, ODT), p2 = column_range(p, n1, n2, MODE, ODT);
       hipLaunchKernelGGL((k_gemm_tiled_256x256<AF, BF, MODE, ODT, PATH>), dim3((unsigned)(ntm * (n1 / 256))),
                          dim3(512), 0, st, p1);
-      hipLaunchKernelGGL((k_gemm_tiled_256x192<AF, BF, MODE, ODT, PATH>), dim3((unsigned)(ntm * ((n2 + 191) / 192))),
-                         dim3(512), 0, st, p2);
+      if constexpr (ODT < ODT_Q_E4M3)
+        hipLaunchKernelGGL((k_gemm_tiled_256x192<AF, BF, MODE, ODT, PATH>),
+                           dim3((unsigned)(ntm * ((n2 + 191) / 192))), dim3(512), 0, st, p2);
       return;
     }
   }
@@ -476,7 +544,9 @@ static void tiled_path(const GemmArgs& p, int path, hipStream_t st) {
 template <int AF, int BF, int MODE>
 static void tiled_odt(const GemmArgs& p, int odt, int path, hipStream_t st) {
   if (odt == DT_F32) tiled_path<AF, BF, MODE, DT_F32>(p, path, st);
-  else tiled_path<AF, BF, MODE, DT_BF16>(p, path, st);
+  else if (odt == DT_BF16) tiled_path<AF, BF, MODE, DT_BF16>(p, path, st);
+  else if (odt == ODT_Q_E4M3) tiled_path<AF, BF, MODE, ODT_Q_E4M3>(p, path, st);
+  else tiled_path<AF, BF, MODE, ODT_Q_E5M2>(p, path, st);
 }
 
 template <int AF, int BF>

@@ -15,13 +15,17 @@ enum { MODE_EPILOGUE = 0, MODE_PROMOTE = 1, MODE_MX = 2 };
 // Matrix-core path: exact products with fp32 sums (bf16 instructions on the
 // expanded codes), or the FP8 instructions' own accumulation.
 enum { PATH_EXACT = 0, PATH_FAST = 1 };
+// GEMM output kinds beyond the public DT_F32 / DT_BF16: the result quantized
+// in the epilogue to FP8 codes with one fp32 scale per 1x128 tile of a row.
+enum { ODT_Q_E4M3 = 2, ODT_Q_E5M2 = 3 };
 
 struct GemmArgs {
   const uint8_t* a;   // [M, K] codes
   const uint8_t* b;   // [N, K] codes
   const void* sa;     // scales of a (layout per granularity)
   const void* sb;     // scales of b
-  void* out;          // [M, N]
+  void* out;          // [M, N] values, or codes for the quantized outputs
+  float* out_scales;  // quantized outputs: [M, N/128] fp32 tile scales
   int64_t M, N, K;
   int64_t ldo;        // elements between consecutive rows of out (>= N)
   int a_per_row;      // epilogue mode: 1 = one scale per row of a, 0 = one per tensor
@@ -35,6 +39,7 @@ hipError_t launch_dequantize(const uint8_t* q, const void* scales, int64_t rows,
                              void* y, int odt, hipStream_t st);
 hipError_t launch_gemm_tiled(const GemmArgs& p, int afmt, int bfmt, int mode, int odt, int path, hipStream_t st);
 hipError_t launch_gemm_skinny(const GemmArgs& p, int afmt, int bfmt, int mode, int odt, int path, hipStream_t st);
-hipError_t launch_fill_zero(void* out, int64_t bytes, hipStream_t st);
+hipError_t launch_fill_zero(void* out, int64_t bytes, hipStream_t st);     // bytes % 4 == 0, 4-byte aligned
+hipError_t launch_fill_f32(float* out, int64_t n, float v, hipStream_t st);
 
 }  // namespace fp8blk

@@ -199,6 +199,29 @@ fp8_status_t fp8_gemm_blockscaled_ex(const uint8_t* a, fp8_format_t a_fmt, fp8_g
                                      void* out, fp8_dtype_t out_dt, fp8_gemm_algo_t algo,
                                      fp8_accum_t accum, hipStream_t stream);
 
+/* Block-scaled FP8 GEMM whose result leaves the kernel already quantized for
+ * the next layer ("Illustrated GPU kernels, Part 8", the fourth of its five
+ * closing rules: quantize in the epilogue of the kernel that produces the
+ * tensor, where the per-block amax is a reduction over values already in
+ * registers; "The FP8 Family", DeepSeek-V3 callout: 1x128 activation tiles).
+ * Operands, scale pairs, shapes and accum are as for fp8_gemm_blockscaled_ex.
+ * The fp32 result (bit for bit the values an FP8_DT_F32 call with the same
+ * accum writes) is quantized per row and 128 output columns to out_fmt exactly
+ * as fp8_quantize does with FP8_GRAN_TILE_1x128:
+ *   out_codes   uint8 [M, N]      one code per element
+ *   out_scales  fp32 [M, N/128]   s = RN32(amax / Vmax) of each row tile
+ * so (out_codes, out_scales) can be the next GEMM's a / a_scales directly.
+ * Requires N % 128 == 0 (FP8_ERR_SHAPE otherwise); out_codes 16-byte and
+ * out_scales 4-byte aligned.  K == 0 writes zero codes and scales of 1.
+ * Always runs the tiled kernel. */
+fp8_status_t fp8_gemm_blockscaled_quant(const uint8_t* a, fp8_format_t a_fmt, fp8_granularity_t a_g,
+                                        const void* a_scales,
+                                        const uint8_t* b, fp8_format_t b_fmt, fp8_granularity_t b_g,
+                                        const void* b_scales,
+                                        int64_t M, int64_t N, int64_t K,
+                                        fp8_format_t out_fmt, uint8_t* out_codes, float* out_scales,
+                                        fp8_accum_t accum, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

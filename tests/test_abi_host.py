@@ -111,3 +111,18 @@ def test_gemm_validation(lib):
     assert g(*args(T, T, od=3)) == 2
     assert g(*args(T, T, acc=2)) == 2
     assert g(*args(T, T, M=0)) == 0          # empty output: nothing to do
+
+
+def test_gemm_quant_validation(lib):
+    g = lib.fp8_gemm_blockscaled_quant
+    T, TL, BL = fb.GRAN_TENSOR, fb.GRAN_TILE_1x128, fb.GRAN_BLOCK_128x128
+    args = lambda ag, bg, M=32, N=256, K=256, fmt=0, codes=FAKE, scales=FAKE: (
+        FAKE, 0, ag, FAKE, FAKE, 0, bg, FAKE, M, N, K, fmt, codes, scales, 0, None)
+    assert g(*args(T, T, N=144)) == 3          # N % 128 for the 1x128 output tiles
+    assert g(*args(T, T, fmt=2)) == 2          # output format
+    assert g(*args(TL, TL)) == 4               # unsupported pair
+    assert g(*args(T, T, codes=None)) == 1
+    assert g(*args(T, T, scales=FAKE + 2)) == 7
+    assert g(*args(T, T, codes=FAKE + 8)) == 7
+    assert g(*args(TL, BL, M=0)) == 0          # empty output: nothing to do
+
