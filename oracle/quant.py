@@ -176,3 +176,46 @@ def to_bf16_bits(y: np.ndarray) -> np.ndarray:
 
 def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---- delayed scaling --------------------------------------------------------
+# "FP8 Mixed-Precision Serving", section "Quantization Granularity and Scaling
+# Topologies", delayed scaling: the scale of a per-tensor quantization comes
+# from a rolling history H of the amax of earlier iterations (length l, e.g.
+# 1024), rho = FP8max / (2^m max(H)) with a safety margin m, instead of from the
+# current tensor; the current tensor's amax then enters the history.  Stored
+# as the dequant multiplier s = 1 / rho = 2^m max(H) / Vmax (reading G2).
+
+
+def delayed_scale(history: np.ndarray, margin: int, fmt) -> np.float32:
+    """s = RN32(2^m * max(H) / Vmax), 1 when that is 0; NaN entries are ignored."""
+    h = np.asarray(history, dtype=np.float32).astype(np.float64).reshape(-1)
+    h = h[~np.isnan(h)]
+    amax = float(h.max()) if h.size else 0.0
+    f = formats.fmt_of(fmt)
+    with np.errstate(over="ignore"):
+        s = np.float32(np.ldexp(amax, margin) / f.vmax)
+    return np.float32(1.0) if s == 0 else s
+
+
+def quantize_with_scale(x: np.ndarray, s, fmt) -> np.ndarray:
+    """Codes of x under a given fp32 scale: sat_rne(RN32(x / s))."""
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    with np.errstate(over="ignore"):
+        q32 = (x64 / np.float64(np.float32(s))).astype(np.float32)
+    return formats.encode(q32.astype(np.float64), fmt)
+
+
+def quantize_delayed(x: np.ndarray, history: np.ndarray, pos: int, margin: int, fmt):
+    """One iteration of delayed scaling on a tensor: the scale from the history
+    as it stands, the codes under that scale (values beyond s*Vmax saturate),
+    and the history with entry pos replaced by the tensor's amax.
+    Returns (codes, s, new_history)."""
+    s = delayed_scale(history, margin, fmt)
+    codes = quantize_with_scale(x, s, fmt)
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.abs(x32).max()) if x32.size else np.float32(0.0)
+    new_h = np.asarray(history, dtype=np.float32).copy()
+    new_h[pos] = amax
+    return codes, s, new_h
+

@@ -213,3 +213,56 @@ def test_input_generator_is_deterministic():
     xf = workloads.draw_x(wl, 64, 512, np.random.default_rng(wl.seed))
     tb = torch.from_numpy(xf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(workloads.f32_to_bf16_bits(xf), tb)
+
+
+# ---- delayed scaling ("FP8 Mixed-Precision Serving", delayed scaling) --------
+
+def test_delayed_scale_closed_forms():
+    E4M3, E5M2 = 0, 1
+    assert quant.delayed_scale(np.zeros(4, np.float32), 0, E4M3) == np.float32(1.0)   # empty history
+    assert quant.delayed_scale(np.array([1.0, 448.0, 3.0], np.float32), 0, E4M3) == np.float32(1.0)
+    assert quant.delayed_scale(np.array([1.0, 448.0, 3.0], np.float32), 2, E4M3) == np.float32(4.0)
+    assert quant.delayed_scale(np.array([57344.0], np.float32), 0, E5M2) == np.float32(1.0)
+    assert quant.delayed_scale(np.array([np.nan, 896.0], np.float32), 0, E4M3) == np.float32(2.0)
+
+
+def test_delayed_scale_is_correctly_rounded():
+    """Against exact rational arithmetic: s = RN32(2^m max(H) / Vmax)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    for _ in range(500):
+        h = (rng.random(8) * 10.0 ** rng.integers(-30, 30)).astype(np.float32)
+        m = int(rng.integers(0, 8))
+        exact = Fraction(float(h.max())) * 2 ** m / 448
+        s = quant.delayed_scale(h, m, 0)
+        lo, hi = np.nextafter(s, np.float32(0)), np.nextafter(s, np.float32(np.inf))
+        # s is the nearest fp32 to the exact quotient
+        assert abs(Fraction(float(s)) - exact) <= abs(Fraction(float(lo)) - exact)
+        assert abs(Fraction(float(s)) - exact) <= abs(Fraction(float(hi)) - exact)
+
+
+def test_quantize_delayed_saturates_and_updates_history():
+    """A spike larger than the history allows clips to +-Vmax (the overflow
+    risk the page names); the history entry then holds the spike's amax."""
+    h = np.array([2.0, 1.0, 0.0], np.float32)
+    x = np.array([[0.5, -1.0, 2.0, 50.0, -50.0, 0.0, 1.5, -2.0]], np.float32)
+    codes, s, h2 = quant.quantize_delayed(x, h, 2, 0, 0)
+    assert s == np.float32(2.0 / 448.0)
+    assert codes[0, 3] == 0x7E and codes[0, 4] == 0xFE          # +-448 after saturation
+    assert codes[0, 2] == 0x7E                                    # 2.0 / s = 448 exactly
+    assert h2.tolist() == [2.0, 1.0, 50.0] and h.tolist() == [2.0, 1.0, 0.0]
+    # with the current scale the same tensor would not clip
+    xp = np.zeros((1, 128), np.float32)
+    xp[:, :8] = x
+    q_cur, s_cur = quant.quantize(xp, quant.TENSOR, 0)
+    assert s_cur[0] == np.float32(50.0 / 448.0) and q_cur[0, 3] == 0x7E
+
+
+def test_delayed_equals_current_scaling_when_history_holds_the_amax():
+    """With max(H) = amax(x) and no margin the delayed codes are the per-tensor ones."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((4, 256)).astype(np.float32)
+    h = np.array([np.abs(x).max(), 0.5], np.float32)
+    codes, s, _ = quant.quantize_delayed(x, h, 1, 0, 0)
+    q_cur, s_cur = quant.quantize(x, quant.TENSOR, 0)
+    assert s == s_cur[0] and np.array_equal(codes, q_cur)
