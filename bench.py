@@ -367,6 +367,22 @@ def main(argv=None) -> int:
                                                          stream=stream))
     dq_ms = kernel_ms(lambda st: fb.fp8_dequantize(st[2], st[4], wl.x_fmt, wl.x_gran, wl.in_dtype, y=st[7],
                                                    stream=stream))
+    # Delayed scaling of X as a whole tensor (scale from an amax history of
+    # 16 iterations): one read of the input, against the two reads of
+    # current per-tensor scaling.
+    hist = torch.zeros(16, dtype=torch.float32, device=dev)
+    dsc = torch.empty(1, dtype=torch.float32, device=dev)
+    wsd = torch.empty(max(1, fb.fp8_quantize_workspace_bytes(M, K, fb.GRAN_TENSOR)), dtype=torch.uint8, device=dev)
+    cnt = [0]
+
+    def delayed(st):
+        cnt[0] += 1
+        fb.fp8_quantize_delayed(st[0], wl.x_fmt, hist, cnt[0] % 16, q=st[2], scale=dsc, workspace=wsd, stream=stream)
+
+    qd_ms = kernel_ms(delayed)
+    qd_bytes = M * K * ((2 if wl.in_dtype == workloads.DT_BF16 else 4) + 1) + 8
+    qd_gbs = qd_bytes / (qd_ms * 1e-3) / 1e9
+
     # The next row of the path: the GEMM with its output quantized in the
     # epilogue (E4M3 codes + 1x128 tile scales), against the GEMM followed by
     # a separate quantize of its output.
@@ -435,6 +451,8 @@ def main(argv=None) -> int:
             "quantize_w_in_step": w_in_step,
             "dequantize_x_ms": round(dq_ms, 4), "dequantize_x_gbs": round(dq_gbs, 1),
             "dequantize_x_frac_hbm": round(dq_gbs / PEAK_HBM_GBS, 4),
+            "quantize_x_delayed_ms": round(qd_ms, 4), "quantize_x_delayed_gbs": round(qd_gbs, 1),
+            "quantize_x_delayed_frac_hbm": round(qd_gbs / PEAK_HBM_GBS, 4),
             "fused_epilogue_quantize": fused,
         },
         "wall_s_timed": round(wall, 4),

@@ -41,6 +41,9 @@ _SIGS = {
     "fp8_quantize_workspace_bytes": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int]),
     "fp8_quantize": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int, _c.c_int,
                                 _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "fp8_quantize_delayed": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p,
+                                        _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_void_p,
+                                        _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "fp8_dequantize": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int, _c.c_int,
                                   _c.c_void_p, _c.c_int, _c.c_void_p]),
     "fp8_cast": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_void_p]),
@@ -165,6 +168,29 @@ def fp8_quantize(x, fmt: int, gran: int, q=None, scales=None, workspace=None, st
                           _ptr(workspace), wsb, _stream(stream))
     _check("fp8_quantize", st)
     return q, scales
+
+
+def fp8_quantize_delayed(x, fmt: int, history, hist_pos: int, margin: int = 0, q=None, scale=None, workspace=None,
+                         stream=None):
+    """Delayed scaling: quantize x (2-D) with the scale from the amax history
+    (device float32 [l]), then store x's amax at history[hist_pos].
+    Returns (codes uint8, scale float32 [1])."""
+    torch = _torch()
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    lib = load_library()
+    ws = lib.fp8_quantize_workspace_bytes(rows, cols, GRAN_TENSOR)
+    if ws and workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=x.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.fp8_quantize_delayed(x.data_ptr(), _dt_of(x), rows, cols, fmt, history.data_ptr(), history.numel(),
+                                  hist_pos, margin, q.data_ptr(), scale.data_ptr(), _ptr(workspace), wsb,
+                                  _stream(stream))
+    _check("fp8_quantize_delayed", st)
+    return q, scale
 
 
 def fp8_dequantize(q, scales, fmt: int, gran: int, out_dtype: int = DT_F32, y=None, stream=None):

@@ -83,6 +83,27 @@ fp8_status_t fp8_quantize(const void* x, fp8_dtype_t x_dt, int64_t rows, int64_t
   return hip_status(launch_quantize(x, (int)x_dt, rows, cols, (int)fmt, (int)g, q, scales, workspace, stream));
 }
 
+fp8_status_t fp8_quantize_delayed(const void* x, fp8_dtype_t x_dt, int64_t rows, int64_t cols, fp8_format_t fmt,
+                                  float* history, int64_t hist_len, int64_t hist_pos, int margin, uint8_t* q,
+                                  float* scale, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dt(x_dt) || !valid_fmt(fmt)) return FP8_ERR_ENUM;
+  const fp8_status_t sh = check_operand(rows, cols, FP8_GRAN_TENSOR);
+  if (sh != FP8_OK) return sh;
+  if (hist_len < 1 || hist_len > (int64_t(1) << 30) || hist_pos < 0 || hist_pos >= hist_len) return FP8_ERR_SHAPE;
+  if (margin < 0 || margin > 31) return FP8_ERR_SHAPE;
+  const int64_t total = rows * cols;
+  if (!history || !scale) return FP8_ERR_NULL;
+  if (!aligned(history, 4) || !aligned(scale, 4)) return FP8_ERR_ALIGN;
+  if (total > 0) {
+    if (!x || !q) return FP8_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(q, 16)) return FP8_ERR_ALIGN;
+    if (!workspace || ws_bytes < sizeof(float) * (size_t)kTensorPartials) return FP8_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return FP8_ERR_ALIGN;
+  }
+  return hip_status(launch_quantize_delayed(x, (int)x_dt, total, (int)fmt, history, hist_len, hist_pos, margin, q,
+                                            scale, workspace, stream));
+}
+
 fp8_status_t fp8_dequantize(const uint8_t* q, const void* scales, int64_t rows, int64_t cols, fp8_format_t fmt,
                             fp8_granularity_t g, void* y, fp8_dtype_t y_dt, hipStream_t stream) {
   if (!valid_dt(y_dt) || !valid_fmt(fmt) || !valid_gran(g)) return FP8_ERR_ENUM;

@@ -9,7 +9,7 @@ namespace fp8blk {
 
 // Number of per-workgroup partial maxima of the per-tensor amax pass; the
 // per-tensor quantize needs kTensorPartials floats of workspace.
-constexpr int kTensorPartials = 1024;
+constexpr int kTensorPartials = 8192;
 
 enum { MODE_EPILOGUE = 0, MODE_PROMOTE = 1, MODE_MX = 2 };
 // Matrix-core path: exact products with fp32 sums (bf16 instructions on the
@@ -34,6 +34,10 @@ struct GemmArgs {
 
 hipError_t launch_quantize(const void* x, int dt, int64_t rows, int64_t cols, int fmt, int g, uint8_t* q,
                            void* scales, void* ws, hipStream_t st);
+// Delayed scaling of a whole tensor of `total` elements (total % 8 == 0):
+// scale[0] from hist[0..len), codes under it, then hist[pos] = amax.
+hipError_t launch_quantize_delayed(const void* x, int dt, int64_t total, int fmt, float* hist, int64_t len,
+                                   int64_t pos, int margin, uint8_t* q, float* scale, void* ws, hipStream_t st);
 hipError_t launch_cast(const void* x, int dt, int64_t n, int fmt, uint8_t* q, hipStream_t st);
 hipError_t launch_dequantize(const uint8_t* q, const void* scales, int64_t rows, int64_t cols, int fmt, int g,
                              void* y, int odt, hipStream_t st);

@@ -207,6 +207,112 @@ __global__ __launch_bounds__(256) void k_quant_tensor(const void* __restrict__ x
 
 __global__ void k_fill_f32(float* p, float v) { *p = v; }
 
+// ---- delayed scaling ----------------------------------------------------------
+// ("FP8 Mixed-Precision Serving", section "Quantization Granularity and
+// Scaling Topologies", delayed scaling.)  The scale comes from the amax
+// history of earlier iterations, s = RN32(max(H) / (Vmax 2^-m)) = the inverse
+// of rho = FP8max / (2^m max(H)); the tensor is encoded under it in one pass
+// that also reduces its own amax, which then replaces history entry pos.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_delayed_scale(const float* __restrict__ hist, int64_t len, int margin,
+                                                        float* __restrict__ scale) {
+  __shared__ float red[16];
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < len; i += 256) m = fmaxf(m, hist[i]);  // fmaxf skips NaN entries
+  m = block_max(m, red);
+  if (threadIdx.x == 0) {
+    const float s = m / __builtin_amdgcn_ldexpf(Fp8Limits<FMT>::vmax, -margin);  // correctly rounded
+    *scale = s == 0.0f ? 1.0f : s;
+  }
+}
+
+// Encodes under the history's scale and reduces the tensor's amax per wave
+// (no LDS, no barrier).  With a short history (FOLD) every wave derives the
+// scale itself from the history, which saves the separate scale kernel's
+// launch; the first wave writes it out.  Each thread keeps 4 chunks of loads
+// in flight.  partial[] holds one maximum per wave.
+template <int FMT, int DT, bool FOLD>
+__global__ __launch_bounds__(256) void k_quant_given_scale(const void* __restrict__ x, uint8_t* __restrict__ q,
+                                                            float* __restrict__ scale, const float* __restrict__ hist,
+                                                            int64_t len, int margin, int64_t nch,
+                                                            float* __restrict__ partial) {
+  const int lane = threadIdx.x & 63;
+  float s;
+  if constexpr (FOLD) {
+    float hm = 0.0f;
+    for (int64_t i = lane; i < len; i += 64) hm = fmaxf(hm, hist[i]);  // fmaxf skips NaN entries
+    hm = wave_max(hm);
+    const float sv = hm / __builtin_amdgcn_ldexpf(Fp8Limits<FMT>::vmax, -margin);  // correctly rounded
+    s = sv == 0.0f ? 1.0f : sv;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
+  } else {
+    s = *scale;
+  }
+  float m = 0.0f;
+  const int64_t G = (int64_t)gridDim.x * 256;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < nch; idx += 4 * G) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (idx + u * G < nch) load8<DT>(x, 8 * (idx + u * G), v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (idx + u * G < nch) {
+        m = fmaxf(m, local_amax<8>(v[u]));
+        uint32_t out[2];
+        encode_scaled<FMT, 8>(v[u], s, out);
+        *reinterpret_cast<u32x2*>(q + 8 * (idx + u * G)) = u32x2{out[0], out[1]};
+      }
+    }
+  }
+  m = wave_max(m);
+  if (lane == 0) partial[blockIdx.x * 4 + (threadIdx.x >> 6)] = m;
+}
+
+__global__ __launch_bounds__(256) void k_partials_to_slot(const float* __restrict__ partial, int npartial,
+                                                           float* __restrict__ slot) {
+  __shared__ float red[16];
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < npartial; i += 256) m = fmaxf(m, partial[i]);
+  m = block_max(m, red);
+  if (threadIdx.x == 0) *slot = m;
+}
+
+template <int FMT, int DT>
+static void quantize_delayed_t(const void* x, int64_t total, float* hist, int64_t len, int64_t pos, int margin,
+                               uint8_t* q, float* scale, float* partial, hipStream_t st) {
+  constexpr int64_t kFoldLen = 4096;   // history read by every workgroup up to this length
+  if (total == 0 || len > kFoldLen)
+    hipLaunchKernelGGL((k_delayed_scale<FMT>), dim3(1), dim3(256), 0, st, hist, len, margin, scale);
+  if (total == 0) {
+    hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(1), 0, st, hist + pos, 0.0f);
+    return;
+  }
+  const int64_t nch = total / 8;
+  int64_t p = (nch + 2047) / 2048;   // 8 chunks of 8 elements per thread
+  if (p > kTensorPartials / 4) p = kTensorPartials / 4;   // one partial per wave
+  if (len > kFoldLen)
+    hipLaunchKernelGGL((k_quant_given_scale<FMT, DT, false>), dim3((unsigned)p), dim3(256), 0, st, x, q, scale, hist,
+                       len, margin, nch, partial);
+  else
+    hipLaunchKernelGGL((k_quant_given_scale<FMT, DT, true>), dim3((unsigned)p), dim3(256), 0, st, x, q, scale, hist,
+                       len, margin, nch, partial);
+  hipLaunchKernelGGL(k_partials_to_slot, dim3(1), dim3(256), 0, st, partial, (int)(4 * p), hist + pos);
+}
+
+hipError_t launch_quantize_delayed(const void* x, int dt, int64_t total, int fmt, float* hist, int64_t len,
+                                   int64_t pos, int margin, uint8_t* q, float* scale, void* ws, hipStream_t st) {
+  float* partial = reinterpret_cast<float*>(ws);
+  if (fmt == FMT_E4M3) {
+    if (dt == DT_BF16) quantize_delayed_t<FMT_E4M3, DT_BF16>(x, total, hist, len, pos, margin, q, scale, partial, st);
+    else quantize_delayed_t<FMT_E4M3, DT_F32>(x, total, hist, len, pos, margin, q, scale, partial, st);
+  } else {
+    if (dt == DT_BF16) quantize_delayed_t<FMT_E5M2, DT_BF16>(x, total, hist, len, pos, margin, q, scale, partial, st);
+    else quantize_delayed_t<FMT_E5M2, DT_F32>(x, total, hist, len, pos, margin, q, scale, partial, st);
+  }
+  return hipGetLastError();
+}
+
 // ---- unscaled cast, defined for every input ---------------------------------
 template <int FMT>
 __device__ __forceinline__ uint32_t cast_special_fix(float v, uint32_t code) {

@@ -122,7 +122,7 @@ int fp8_abi_version(void);
 
 /* Device workspace fp8_quantize needs for this shape and granularity, in
  * bytes.  Non-zero only for FP8_GRAN_TENSOR (per-workgroup partial maxima of
- * the amax pass, at most 4 KiB).  Returns 0 for invalid arguments. */
+ * the amax pass, at most 32 KiB).  Returns 0 for invalid arguments. */
 size_t fp8_quantize_workspace_bytes(int64_t rows, int64_t cols, fp8_granularity_t g);
 
 /* Quantize a [rows, cols] operand with current (just-in-time) scaling.
@@ -145,6 +145,28 @@ fp8_status_t fp8_quantize(const void* x, fp8_dtype_t x_dt, int64_t rows, int64_t
                           fp8_format_t fmt, fp8_granularity_t g,
                           uint8_t* q, void* scales, void* workspace, size_t ws_bytes,
                           hipStream_t stream);
+
+/* Quantize a whole [rows, cols] tensor with delayed scaling ("FP8
+ * Mixed-Precision Serving", section "Quantization Granularity and Scaling
+ * Topologies", delayed scaling): the scale comes from a history of the amax
+ * of earlier iterations instead of from this tensor, saving the reduction
+ * pass before the encode.
+ *   history   device fp32 [hist_len], caller-owned ring of amax values
+ *             (zero-initialized; NaN entries are ignored)
+ *   scale     device fp32 [1]: written with s = RN32(max(history) * 2^margin /
+ *             Vmax), 1 when that is 0 (the inverse of the page's
+ *             rho = FP8max / (2^m max(H)))
+ *   q         codes under s; values beyond s * Vmax saturate to +-Vmax
+ *   then history[hist_pos] = max |x| of this tensor (the caller advances
+ *   hist_pos, modulo hist_len, between iterations).
+ * 0 <= hist_pos < hist_len, 1 <= hist_len <= 2^30, 0 <= margin <= 31; cols as
+ * for fp8_quantize.  The workspace is as for FP8_GRAN_TENSOR
+ * (fp8_quantize_workspace_bytes(rows, cols, FP8_GRAN_TENSOR)).  Everything
+ * runs on the stream: no host synchronization. */
+fp8_status_t fp8_quantize_delayed(const void* x, fp8_dtype_t x_dt, int64_t rows, int64_t cols,
+                                  fp8_format_t fmt, float* history, int64_t hist_len, int64_t hist_pos,
+                                  int margin, uint8_t* q, float* scale, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /* Dequantize codes back to fp32 or bf16: y = RN32(decode(q) * s) (MX32:
  * decode(q) * 2^e), then rounded to bf16 if y_dt is FP8_DT_BF16.

@@ -49,7 +49,7 @@ def test_status_strings(lib):
 
 
 def test_workspace_query(lib):
-    assert lib.fp8_quantize_workspace_bytes(128, 512, fb.GRAN_TENSOR) == 4096
+    assert lib.fp8_quantize_workspace_bytes(128, 512, fb.GRAN_TENSOR) == 4 * 8192
     for g in (fb.GRAN_ROW, fb.GRAN_TILE_1x128, fb.GRAN_BLOCK_128x128, fb.GRAN_MX32):
         assert lib.fp8_quantize_workspace_bytes(128, 512, g) == 0
     assert lib.fp8_quantize_workspace_bytes(128, 500, fb.GRAN_TENSOR) == 0
@@ -126,3 +126,19 @@ def test_gemm_quant_validation(lib):
     assert g(*args(T, T, codes=FAKE + 8)) == 7
     assert g(*args(TL, BL, M=0)) == 0          # empty output: nothing to do
 
+
+
+def test_quantize_delayed_validation(lib):
+    f = lib.fp8_quantize_delayed
+    args = lambda rows=4, cols=128, fmt=0, hist=FAKE, hl=8, hp=0, m=0, q=FAKE, sc=FAKE, ws=FAKE, wsb=32768: (
+        FAKE, 0, rows, cols, fmt, hist, hl, hp, m, q, sc, ws, wsb, None)
+    assert f(*args(fmt=3)) == 2
+    assert f(*args(cols=100)) == 3            # cols % 128
+    assert f(*args(hp=8)) == 3                # position outside the history
+    assert f(*args(hl=0)) == 3
+    assert f(*args(m=32)) == 3                # margin outside 0..31
+    assert f(*args(hist=None)) == 1
+    assert f(*args(sc=None)) == 1
+    assert f(*args(ws=None)) == 5
+    assert f(*args(wsb=16)) == 5
+    assert f(*args(sc=FAKE + 2)) == 7
