@@ -177,28 +177,46 @@ def _pmc_rows(path: str, counter: str):
     return rows
 
 
-def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel_substr, copy_bytes):
-    """HBM bytes per launch of the kernels whose name contains kernel_substr:
-    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) averaged over its dispatches,
-    each scaled by (known bytes / counter reading) of a plain device copy."""
-    def mean_of(path, counter, pick):
-        vals = [v for n, v in _pmc_rows(path, counter) if pick(n)]
-        if not vals:
-            raise SystemExit(f"no {counter} dispatch of the selected kernel in {path}")
-        return float(np.mean(vals)), len(vals)
+# The GEMM kernels of a plain launch: f32 or bf16 output (the fourth template
+# argument, 0 or 1).  The quantized-output variant (2, 3) is a different launch.
+GEMM_KERNEL_RE = r"k_gemm_\w+<\d+, \d+, \d+, [01],"
 
-    fk, nf = mean_of(fetch_csv, "FETCH_SIZE", lambda n: kernel_substr in n)
-    wk, nw = mean_of(write_csv, "WRITE_SIZE", lambda n: kernel_substr in n)
+
+def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel_re, copy_bytes):
+    """HBM bytes per launch of the kernels whose name matches kernel_re:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) averaged over the dispatches
+    of each distinct kernel, summed over those kernels (one launch runs each of
+    them once: the column split's two tile shapes), each counter scaled by
+    (known bytes / counter reading) of a plain device copy."""
+    import re
+    pat = re.compile(kernel_re)
+
+    def per_kernel(path, counter):
+        by = {}
+        for n, v in _pmc_rows(path, counter):
+            if pat.search(n):
+                by.setdefault(n, []).append(v)
+        if not by:
+            raise SystemExit(f"no {counter} dispatch of the selected kernels in {path}")
+        return {n: float(np.mean(v)) for n, v in by.items()}, sum(len(v) for v in by.values())
+
+    fetch, nf = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, nw = per_kernel(write_csv, "WRITE_SIZE")
+    if set(fetch) != set(write):
+        raise SystemExit("FETCH_SIZE and WRITE_SIZE runs saw different kernels")
+    fk, wk = sum(fetch.values()), sum(write.values())
     # the copy probe's copy is its largest dispatch
     cf = max(v for _, v in _pmc_rows(copy_fetch_csv, "FETCH_SIZE"))
     cw = max(v for _, v in _pmc_rows(copy_write_csv, "WRITE_SIZE"))
     kib = copy_bytes / 1024.0
     ff, fw = kib / cf, kib / cw
     traffic = (fk * ff + wk * fw) * 1024.0
-    return "\n".join([
-        f"kernel_match: {kernel_substr}",
-        f"fetch_kib_per_dispatch: {fk:.1f}   (mean of {nf} dispatches)",
-        f"write_kib_per_dispatch: {wk:.1f}   (mean of {nw} dispatches)",
+    lines = [f"kernel_match: {kernel_re}"]
+    for n in sorted(fetch):
+        lines.append(f"  kernel {n}: fetch_kib {fetch[n]:.1f}, write_kib {write[n]:.1f} (mean per dispatch)")
+    lines += [
+        f"fetch_kib_per_launch: {fk:.1f}   ({len(fetch)} kernel(s), {nf} dispatches)",
+        f"write_kib_per_launch: {wk:.1f}   ({len(write)} kernel(s), {nw} dispatches)",
         f"copy_bytes: {copy_bytes}",
         f"copy_fetch_kib: {cf:.1f}",
         f"copy_write_kib: {cw:.1f}",
@@ -206,7 +224,8 @@ def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kern
         f"write_factor: {fw:.4f}",
         f"traffic_bytes_per_launch: {traffic:.0f}",
         f"source_sha256: {gemm_source_hash()}",
-    ])
+    ]
+    return "\n".join(lines)
 
 
 def main(argv=None) -> int:
@@ -227,7 +246,8 @@ def main(argv=None) -> int:
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                                                                 "COPY_WRITE_CSV"),
                     help="print the calibrated HBM traffic of the GEMM kernel and exit")
-    ap.add_argument("--kernel-match", default="k_gemm_", help="kernel-name substring for --summarize-traffic")
+    ap.add_argument("--kernel-match", default=GEMM_KERNEL_RE,
+                    help="kernel-name regular expression for --summarize-traffic")
     args = ap.parse_args(argv)
 
     if args.summarize_trace:

@@ -44,17 +44,22 @@ def _csv(path, rows):
 
 def test_traffic_summary_calibration(tmp_path):
     kib = bench.COPY_PROBE_BYTES / 1024
-    _csv(tmp_path / "f.csv", [("k_gemm_a", "FETCH_SIZE", 100.0), ("k_gemm_a", "FETCH_SIZE", 300.0),
-                              ("other", "FETCH_SIZE", 9e9)])
-    _csv(tmp_path / "w.csv", [("k_gemm_a", "WRITE_SIZE", 50.0), ("k_gemm_a", "WRITE_SIZE", 50.0)])
+    big, split, quant = ("k_gemm_tiled_256x256<0, 0, 1, 1, 0>(args)", "k_gemm_tiled_256x192<0, 0, 1, 1, 0>(args)",
+                         "k_gemm_tiled_256x256<0, 0, 1, 2, 0>(args)")
+    _csv(tmp_path / "f.csv", [(big, "FETCH_SIZE", 100.0), (split, "FETCH_SIZE", 30.0), (big, "FETCH_SIZE", 300.0),
+                              (split, "FETCH_SIZE", 10.0), (quant, "FETCH_SIZE", 7e6), ("other", "FETCH_SIZE", 9e9)])
+    _csv(tmp_path / "w.csv", [(big, "WRITE_SIZE", 50.0), (split, "WRITE_SIZE", 5.0), (big, "WRITE_SIZE", 50.0),
+                              (split, "WRITE_SIZE", 15.0), (quant, "WRITE_SIZE", 3e6)])
     _csv(tmp_path / "cf.csv", [("fill", "FETCH_SIZE", 1.0), ("copy", "FETCH_SIZE", kib / 2)])
     _csv(tmp_path / "cw.csv", [("copy", "WRITE_SIZE", kib)])
     text = bench.summarize_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(tmp_path / "cf.csv"),
-                                   str(tmp_path / "cw.csv"), "k_gemm_", bench.COPY_PROBE_BYTES)
-    kv = dict(line.split(":", 1) for line in text.splitlines())
-    # fetch counter reads half the copy: factor 2; mean fetch 200 KiB -> 400 KiB; writes 50 KiB
+                                   str(tmp_path / "cw.csv"), bench.GEMM_KERNEL_RE, bench.COPY_PROBE_BYTES)
+    kv = dict(line.split(":", 1) for line in text.splitlines() if not line.startswith(" "))
+    # fetch counter reads half the copy: factor 2.  One launch = one dispatch of
+    # each tile shape: fetch (200 + 20) KiB -> 440 KiB; writes 50 + 10 KiB.  The
+    # quantized-output kernel and unrelated kernels are not part of it.
     assert float(kv["fetch_factor"].split()[0]) == pytest.approx(2.0)
-    assert float(kv["traffic_bytes_per_launch"]) == pytest.approx((400 + 50) * 1024)
+    assert float(kv["traffic_bytes_per_launch"]) == pytest.approx((440 + 60) * 1024)
     assert kv["source_sha256"].strip() == bench.gemm_source_hash()
 
 
