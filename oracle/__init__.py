@@ -9,7 +9,9 @@ Contents
   formats  -- E4M3 / E5M2 decode and the saturating round-to-nearest-even cast
               (two independent encoders: nearest-value search and binade rounding)
   quant    -- scale granularities, amax, fp32 and E8M0 scale rules, quantize,
-              dequantize
+              dequantize, delayed scaling, and the FP8 KV-cache codec
+              (quantize on append, dequantize on read, static scales per
+              tensor / head / channel)
   gemm     -- exact (fp64) GEMM on the dequantized operands, |x|.|w| bound and the
               elementwise tolerance test
 

@@ -35,6 +35,8 @@ What is computed, with where the pages say it:
     the definition used here).
   * rows, K must be positive multiples as the layouts need: K % 128 == 0 in all
     modes, rows % 128 == 0 for BLOCK_128x128 (partial groups are rejected).
+  * with a given scale (delayed scaling, the KV cache) the quotient x / s can
+    exceed the fp32 range; clip(round(x / s)) then still saturates to +-Vmax.
 """
 
 from __future__ import annotations
@@ -201,8 +203,14 @@ def delayed_scale(history: np.ndarray, margin: int, fmt) -> np.float32:
 def quantize_with_scale(x: np.ndarray, s, fmt) -> np.ndarray:
     """Codes of x under a given fp32 scale: sat_rne(RN32(x / s))."""
     x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    q64 = x64 / np.asarray(s, dtype=np.float32).astype(np.float64)
     with np.errstate(over="ignore"):
-        q32 = (x64 / np.float64(np.float32(s))).astype(np.float32)
+        q32 = q64.astype(np.float32)
+    # The quotient of finite x by a positive s is a finite real; where its fp32
+    # rounding overflows it lies far beyond Vmax, so the code saturates
+    # (reading G21) rather than becoming an E5M2 Inf.
+    big = np.float32(np.finfo(np.float32).max)
+    q32 = np.where(np.isinf(q32) & np.isfinite(q64), np.where(q64 < 0, -big, big), q32).astype(np.float32)
     return formats.encode(q32.astype(np.float64), fmt)
 
 
@@ -219,3 +227,68 @@ def quantize_delayed(x: np.ndarray, history: np.ndarray, pos: int, margin: int, 
     new_h[pos] = amax
     return codes, s, new_h
 
+
+
+# ---- FP8 KV cache ------------------------------------------------------------
+# "FP8 Mixed-Precision Serving", section "FP8 KV Cache Architecture and Serving
+# Latency": key and value states stored as E4M3 codes (one byte per element,
+# half of bf16), with the cache size 2 * B * L * N_heads * D_head * bytes per
+# layer.  "FP8 Serving" (the quality table and "Things to try"): a per-tensor
+# scale, a per-channel one for channel-structured outliers, and E5M2 as the
+# format with more range.  The scales are static (given by the caller); the
+# cache is a pool of token slots, each holding one token's [heads, head_dim]
+# codes, addressed through a slot index per token (paged layouts map their
+# block tables to slots).
+
+KV_SCALE_TENSOR, KV_SCALE_HEAD, KV_SCALE_CHANNEL = 0, 1, 2
+
+
+def kv_cache_bytes(batch: int, seq_len: int, heads: int, head_dim: int, bytes_per_element: int,
+                   layers: int = 1) -> int:
+    """Memory_KV = 2 * B * L * N_heads * D_head * BytesPerElement, times layers."""
+    return 2 * batch * seq_len * heads * head_dim * bytes_per_element * layers
+
+
+def kv_scale_of(scale_kind: int, scales, heads: int, head_dim: int) -> np.ndarray:
+    """The fp32 scale of every element of a slot, [heads, head_dim]: one scale
+    (per tensor), one per head, or one per channel (head, dim)."""
+    s = np.asarray(scales, dtype=np.float32).reshape(-1)
+    if scale_kind == KV_SCALE_TENSOR:
+        return np.full((heads, head_dim), s[0], np.float32)
+    if scale_kind == KV_SCALE_HEAD:
+        return np.repeat(s[:heads, None], head_dim, axis=1).astype(np.float32)
+    if scale_kind == KV_SCALE_CHANNEL:
+        return s[:heads * head_dim].reshape(heads, head_dim).copy()
+    raise ValueError(scale_kind)
+
+
+def kv_append(cache: np.ndarray, x: np.ndarray, slots, scale_kind: int, scales, fmt) -> np.ndarray:
+    """Quantize on append: token t of x [tokens, heads, head_dim] is written as
+    codes sat_rne(RN32(x / s)) into cache[slots[t]]; a slot outside
+    [0, num_slots) leaves the cache untouched (reading G22).  Returns a new
+    cache [num_slots, heads, head_dim]."""
+    out = np.array(cache, dtype=np.uint8, copy=True)
+    slots = np.asarray(slots, dtype=np.int64)
+    tokens, heads, head_dim = x.shape
+    s = kv_scale_of(scale_kind, scales, heads, head_dim)
+    for t in range(tokens):
+        if 0 <= slots[t] < out.shape[0]:
+            out[slots[t]] = quantize_with_scale(x[t], s, fmt)
+    return out
+
+
+def kv_gather(cache: np.ndarray, slots, scale_kind: int, scales, fmt) -> np.ndarray:
+    """Dequantize on read: row i is RN32(decode(cache[slots[i]]) * s) as float32
+    [n, heads, head_dim]; a slot outside [0, num_slots) reads as zeros
+    (reading G22)."""
+    cache = np.asarray(cache, dtype=np.uint8)
+    num_slots, heads, head_dim = cache.shape
+    slots = np.asarray(slots, dtype=np.int64)
+    s = kv_scale_of(scale_kind, scales, heads, head_dim).astype(np.float64)
+    out = np.zeros((len(slots), heads, head_dim), np.float32)
+    for i, slot in enumerate(slots):
+        if 0 <= slot < num_slots:
+            v = formats.decode(cache[slot], fmt) * s
+            with np.errstate(over="ignore", invalid="ignore"):
+                out[i] = v.astype(np.float32)
+    return out
