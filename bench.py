@@ -24,6 +24,13 @@ reads data another launch left in the 256 MB last-level cache.
 For the decode workload (c4_decode_skinny) W is quantized once per input set
 in setup, as a model's weights are, and a step is quantize X + GEMM.
 
+The FP8 KV-cache workload (--workload kv_llama8b_b32_ctx8k: 32 sequences of
+8192 tokens, 8 KV heads of 128, bf16 states, E4M3 codes with per-channel
+scales, a paged pool in random block order) has a step of its own: append
+the keys and the values of every token (quantize on append), then read both
+back to bf16 (dequantize on read); `value` is tokens per second and the
+roofline is the HBM bound of the longer of the two kernels.
+
 Profiling helpers (no GPU needed; they read rocprofv3 output):
     python bench.py --summarize-trace DIR       kernel-trace --stats summary
     python bench.py --summarize-traffic ...     HBM bytes of the GEMM from two
@@ -111,13 +118,14 @@ def cpu_baseline(wl, sample_rows: int):
 
 
 GEMM_SOURCES = ("gemm.hip", "gemm_skinny.hip", "gemm_common.h", "device_common.h", "kernels.h")
+KV_SOURCES = ("kv_cache.hip", "kv_cache.h", "given_scale.h", "gemm_common.h", "device_common.h")
 
 
-def gemm_source_hash() -> str:
-    """SHA-256 over the GEMM kernel sources (counter summaries are valid only for these)."""
+def gemm_source_hash(sources=GEMM_SOURCES) -> str:
+    """SHA-256 over the kernel sources (counter summaries are valid only for these)."""
     import hashlib
     h = hashlib.sha256()
-    for name in GEMM_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "block_scaled_precision_x128_amd", "csrc", name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -127,9 +135,9 @@ def traffic_path(workload: str, accum: str) -> str:
     return os.path.join(ROOT, "profiles", f"traffic_{workload}_{accum}.txt")
 
 
-def read_traffic(workload: str, accum: str):
-    """HBM bytes per GEMM launch from a stored counter summary, or None when
-    there is none or it was taken from other kernel sources."""
+def read_traffic(workload: str, accum: str, sources=GEMM_SOURCES):
+    """HBM bytes per launch from a stored counter summary, or None when there
+    is none or it was taken from other kernel sources."""
     path = traffic_path(workload, accum)
     if not os.path.exists(path):
         return None
@@ -139,7 +147,7 @@ def read_traffic(workload: str, accum: str):
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != gemm_source_hash() or "traffic_bytes_per_launch" not in kv:
+    if kv.get("source_sha256") != gemm_source_hash(sources) or "traffic_bytes_per_launch" not in kv:
         return None
     return int(float(kv["traffic_bytes_per_launch"]))
 
@@ -154,23 +162,26 @@ def _sqlite_db(d: str) -> str:
 
 def summarize_trace(d: str) -> str:
     """Per-kernel call count and mean/total duration from a rocprofv3
-    --kernel-trace --stats database."""
+    --kernel-trace --stats database, one line per kernel and grid size (a
+    kernel launched on problems of different sizes gets a line for each)."""
     import sqlite3
     con = sqlite3.connect(_sqlite_db(d))
-    rows = list(con.execute("select name, total_calls, total_duration, average, percentage from top_kernels"))
-    out = [f"{'calls':>6} {'mean_us':>10} {'total_us':>11} {'pct':>6}  kernel"]
-    for name, calls, tot, avg, pct in rows:
-        # top_kernels durations are in microseconds
-        out.append(f"{calls:6d} {avg:10.2f} {tot:11.1f} {pct:6.2f}  {name}")
+    rows = list(con.execute("select name, grid_x, count(*), sum(duration), avg(duration) from kernels "
+                            "group by name, grid_x order by sum(duration) desc"))
+    total = sum(r[3] for r in rows) or 1
+    out = [f"{'calls':>6} {'mean_us':>10} {'total_us':>11} {'pct':>6} {'grid':>9}  kernel"]
+    for name, grid, calls, tot, avg in rows:
+        # durations are in nanoseconds
+        out.append(f"{calls:6d} {avg / 1e3:10.2f} {tot / 1e3:11.1f} {100 * tot / total:6.2f} {grid:9d}  {name}")
     return "\n".join(out)
 
 
-def _pmc_rows(path: str, counter: str):
+def _pmc_rows(path: str, counter: str, min_grid: int = 0):
     import csv
     rows = []
     with open(path) as f:
         for r in csv.DictReader(f):
-            if r.get("Counter_Name") == counter:
+            if r.get("Counter_Name") == counter and int(float(r.get("Grid_Size") or 0)) >= min_grid:
                 rows.append((r.get("Kernel_Name", ""), float(r["Counter_Value"])))
     if not rows:
         raise SystemExit(f"no {counter} rows in {path}")
@@ -182,7 +193,8 @@ def _pmc_rows(path: str, counter: str):
 GEMM_KERNEL_RE = r"k_gemm_\w+<\d+, \d+, \d+, [01],"
 
 
-def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel_re, copy_bytes):
+def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kernel_re, copy_bytes,
+                      sources=GEMM_SOURCES, min_grid: int = 0):
     """HBM bytes per launch of the kernels whose name matches kernel_re:
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) averaged over the dispatches
     of each distinct kernel, summed over those kernels (one launch runs each of
@@ -193,7 +205,7 @@ def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kern
 
     def per_kernel(path, counter):
         by = {}
-        for n, v in _pmc_rows(path, counter):
+        for n, v in _pmc_rows(path, counter, min_grid):
             if pat.search(n):
                 by.setdefault(n, []).append(v)
         if not by:
@@ -211,7 +223,7 @@ def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kern
     kib = copy_bytes / 1024.0
     ff, fw = kib / cf, kib / cw
     traffic = (fk * ff + wk * fw) * 1024.0
-    lines = [f"kernel_match: {kernel_re}"]
+    lines = [f"kernel_match: {kernel_re}"] + ([f"min_grid: {min_grid}"] if min_grid else [])
     for n in sorted(fetch):
         lines.append(f"  kernel {n}: fetch_kib {fetch[n]:.1f}, write_kib {write[n]:.1f} (mean per dispatch)")
     lines += [
@@ -223,9 +235,150 @@ def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kern
         f"fetch_factor: {ff:.4f}",
         f"write_factor: {fw:.4f}",
         f"traffic_bytes_per_launch: {traffic:.0f}",
-        f"source_sha256: {gemm_source_hash()}",
+        f"source_sha256: {gemm_source_hash(sources)}",
     ]
     return "\n".join(lines)
+
+
+# ---- FP8 KV cache ----------------------------------------------------------
+
+def kv_bytes(wl, op: str) -> int:
+    """Algorithmic bytes of one append or read of every token: the values
+    (bf16/fp32) once, the codes once, 8 bytes of slot per token, the scales."""
+    n = wl.tokens * wl.row
+    val_b = (2 if (wl.in_dtype if op == "append" else wl.out_dtype) == workloads.DT_BF16 else 4)
+    sc = {workloads.KV_SCALE_TENSOR: 1, workloads.KV_SCALE_HEAD: wl.heads,
+          workloads.KV_SCALE_CHANNEL: wl.row}[wl.scale_kind]
+    return n * (val_b + 1) + 8 * wl.tokens + 4 * sc
+
+
+def kv_cpu_baseline(wl, sample_tokens: int):
+    """The oracle on the host: append and read back a sample of tokens, for
+    keys and values; tokens per second."""
+    from oracle import quant as oquant
+    rng = np.random.default_rng(wl.seed)
+    x = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(workloads.draw_kv(wl, sample_tokens, rng)))
+    slots = np.arange(sample_tokens, dtype=np.int64)
+    scales = workloads.kv_scales(wl)
+    cache = np.zeros((sample_tokens, wl.heads, wl.head_dim), np.uint8)
+    t0 = time.perf_counter()
+    c = oquant.kv_append(cache, x, slots, wl.scale_kind, scales, wl.fmt)
+    y = oquant.kv_gather(c, slots, wl.scale_kind, scales, wl.fmt)
+    oquant.to_bf16_bits(y)
+    dt = 2 * (time.perf_counter() - t0)          # keys and values
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{sample_tokens} of {wl.tokens} tokens: oracle append (quantize) and read (dequantize "
+                      f"to bf16) of one tensor, timed {dt / 2:.2f} s and doubled for keys and values; 1 thread"}
+
+
+def bench_kv(args, wl) -> int:
+    import torch
+    import block_scaled_precision_x128_amd as fb
+
+    fb.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    T, H, D = wl.tokens, wl.heads, wl.head_dim
+    pool = workloads.kv_pool_slots(wl)
+    slots = torch.from_numpy(workloads.kv_slots(wl)).to(dev)
+    sig = torch.from_numpy(workloads.kv_sigma(wl)).to(dev)
+    scales = {k: torch.from_numpy(workloads.kv_scales(wl, k)).to(dev)
+              for k in (fb.KV_SCALE_TENSOR, fb.KV_SCALE_HEAD, fb.KV_SCALE_CHANNEL)}
+    sc = scales[wl.scale_kind]
+    # States drawn on the GPU (same distribution as the recipe, torch's stream).
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    in_dt = torch.bfloat16 if wl.in_dtype == workloads.DT_BF16 else torch.float32
+    out_dt = torch.bfloat16 if wl.out_dtype == workloads.DT_BF16 else torch.float32
+    states = [(torch.randn((T, H, D), generator=gen, device=dev) * sig[None]).to(in_dt) for _ in range(2)]
+    caches = [torch.zeros((pool, H, D), dtype=torch.uint8, device=dev) for _ in range(2)]
+    outs = [torch.empty((T, H, D), dtype=out_dt, device=dev) for _ in range(2)]
+
+    def append(i, kind=None):
+        k = wl.scale_kind if kind is None else kind
+        fb.fp8_kv_append(states[i], slots, caches[i], scales[k], wl.fmt, k, stream=stream)
+
+    def read(i, kind=None):
+        k = wl.scale_kind if kind is None else kind
+        fb.fp8_kv_gather(caches[i], slots, scales[k], wl.fmt, k, wl.out_dtype, out=outs[i], stream=stream)
+
+    def step(_):
+        append(0)
+        append(1)
+        read(0)
+        read(1)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    def events_ms(fn, reps):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(20_000_000)       # keep the GPU busy while the launches are queued
+        t0.record(stream)
+        for i in range(reps):
+            fn(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    wall0 = time.perf_counter()
+    ms_step = events_ms(step, args.steps)
+    wall = time.perf_counter() - wall0
+    app_ms = events_ms(lambda i: append(i % 2), args.steps)
+    rd_ms = events_ms(lambda i: read(i % 2), args.steps)
+    per_kind = {}
+    for name, k in (("tensor", fb.KV_SCALE_TENSOR), ("head", fb.KV_SCALE_HEAD), ("channel", fb.KV_SCALE_CHANNEL)):
+        per_kind[name] = {"append_ms": round(events_ms(lambda i: append(i % 2, k), args.steps), 4),
+                          "read_ms": round(events_ms(lambda i: read(i % 2, k), args.steps), 4)}
+    # a decode step: one new token for each sequence
+    last = slots.view(wl.batch, wl.context)[:, -1].contiguous()
+    new = states[0].view(wl.batch, wl.context, H, D)[:, -1].contiguous()
+    dec_ms = events_ms(lambda i: fb.fp8_kv_append(new, last, caches[0], sc, wl.fmt, wl.scale_kind,
+                                                  stream=stream), max(args.steps, 50))
+    # leave the caches as the step writes them
+    step(0)
+    torch.cuda.synchronize()
+
+    app_gbs = kv_bytes(wl, "append") / (app_ms * 1e-3) / 1e9
+    rd_gbs = kv_bytes(wl, "read") / (rd_ms * 1e-3) / 1e9
+    dom = "append" if app_ms >= rd_ms else "read"
+    dom_gbs = app_gbs if dom == "append" else rd_gbs
+    traffic = read_traffic(wl.name, dom, KV_SOURCES)
+    result = {
+        "metric": "FP8 KV-cache tokens/s (append + read of keys and values)",
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic (seeded; bf16 states ~N(0,1) with channel outliers x20, drawn on the GPU)",
+        "config": {"workload": f"{wl.name}: {wl.batch} sequences x {wl.context} tokens, {H} KV heads x {D}, "
+                               f"paged blocks of {wl.block} in random order, pool {pool} slots, E4M3, "
+                               f"per-channel scales, bf16 in and out",
+                   "step": "append keys + append values + read keys + read values (all tokens)",
+                   "cache_bytes_fp8": 2 * pool * wl.row, "cache_bytes_bf16_equivalent": 4 * pool * wl.row},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic},
+        "kernels": {"append_ms": round(app_ms, 4), "append_gbs": round(app_gbs, 1),
+                    "append_frac_hbm": round(app_gbs / PEAK_HBM_GBS, 4),
+                    "read_ms": round(rd_ms, 4), "read_gbs": round(rd_gbs, 1),
+                    "read_frac_hbm": round(rd_gbs / PEAK_HBM_GBS, 4),
+                    "by_scale_kind": per_kind,
+                    "decode_append_us": round(dec_ms * 1e3, 2)},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = kv_cpu_baseline(wl, args.kv_cpu_sample_tokens)
+    print(json.dumps(result), flush=True)
+    return 0
 
 
 def main(argv=None) -> int:
@@ -233,13 +386,15 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c3_deepseek_block", choices=workloads.CONFIG_ORDER)
+    ap.add_argument("--workload", default="c3_deepseek_block",
+                    choices=workloads.CONFIG_ORDER + list(workloads.KV_CONFIGS))
     ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0 = enough for 1 GB)")
     ap.add_argument("--accum", choices=["fp32", "native"], default="fp32",
                     help="GEMM accumulation: exact products with fp32 sums (default) or the FP8 "
                          "instructions' own accumulation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=4096)
+    ap.add_argument("--kv-cpu-sample-tokens", type=int, default=16384)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="print a rocprofv3 kernel-trace summary and exit")
@@ -248,13 +403,18 @@ def main(argv=None) -> int:
                     help="print the calibrated HBM traffic of the GEMM kernel and exit")
     ap.add_argument("--kernel-match", default=GEMM_KERNEL_RE,
                     help="kernel-name regular expression for --summarize-traffic")
+    ap.add_argument("--traffic-sources", choices=["gemm", "kv"], default="gemm",
+                    help="which kernel sources the --summarize-traffic hash covers")
+    ap.add_argument("--min-grid", type=int, default=0,
+                    help="--summarize-traffic: only dispatches of at least this many threads")
     args = ap.parse_args(argv)
 
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
         return 0
     if args.summarize_traffic:
-        print(summarize_traffic(*args.summarize_traffic, args.kernel_match, COPY_PROBE_BYTES))
+        print(summarize_traffic(*args.summarize_traffic, args.kernel_match, COPY_PROBE_BYTES,
+                                KV_SOURCES if args.traffic_sources == "kv" else GEMM_SOURCES, args.min_grid))
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -281,6 +441,9 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n}))
         return 0
+
+    if args.workload in workloads.KV_CONFIGS:
+        return bench_kv(args, workloads.KV_CONFIGS[args.workload])
 
     wl = workloads.CONFIGS[args.workload]
     accum = fb.ACCUM_NATIVE if args.accum == "native" else fb.ACCUM_FP32

@@ -13,6 +13,7 @@ Enum values (same as the C header):
   dtypes         DT_F32 = 0, DT_BF16 = 1
   GEMM kernels   GEMM_AUTO = 0, GEMM_TILED = 1, GEMM_SKINNY = 2
   accumulation   ACCUM_FP32 = 0 (exact products, fp32 sums), ACCUM_NATIVE = 1
+  KV scales      KV_SCALE_TENSOR = 0, KV_SCALE_HEAD = 1, KV_SCALE_CHANNEL = 2
 """
 
 from __future__ import annotations
@@ -26,6 +27,7 @@ GRAN_TENSOR, GRAN_ROW, GRAN_TILE_1x128, GRAN_BLOCK_128x128, GRAN_MX32 = 0, 1, 2,
 DT_F32, DT_BF16 = 0, 1
 GEMM_AUTO, GEMM_TILED, GEMM_SKINNY = 0, 1, 2
 ACCUM_FP32, ACCUM_NATIVE = 0, 1
+KV_SCALE_TENSOR, KV_SCALE_HEAD, KV_SCALE_CHANNEL = 0, 1, 2
 
 FP8_OK = 0
 STATUS_NAMES = {0: "FP8_OK", 1: "FP8_ERR_NULL", 2: "FP8_ERR_ENUM", 3: "FP8_ERR_SHAPE",
@@ -59,6 +61,11 @@ _SIGS = {
                                               _c.c_void_p, _c.c_int, _c.c_int, _c.c_void_p,
                                               _c.c_int64, _c.c_int64, _c.c_int64,
                                               _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
+    "fp8_kv_append": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
+                                 _c.c_void_p, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int64,
+                                 _c.c_void_p]),
+    "fp8_kv_gather": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_int64,
+                                 _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -248,3 +255,38 @@ def fp8_gemm_blockscaled_quant(a, a_fmt: int, a_gran: int, a_scales, b, b_fmt: i
         M, N, K, out_fmt, codes.data_ptr(), scales.data_ptr(), accum, _stream(stream))
     _check("fp8_gemm_blockscaled_quant", st)
     return codes, scales
+
+
+def fp8_kv_append(x, slots, cache, scales, fmt: int, scale_kind: int, stream=None):
+    """Quantize on append: x [tokens, heads, head_dim] (fp32 or bf16; the
+    leading dimension may be strided, e.g. a slice of a fused QKV output)
+    written as codes into cache [num_slots, heads, head_dim] at rows slots
+    (int64 [tokens]; slots outside the pool are skipped).  Returns cache."""
+    tokens, heads, head_dim = x.shape
+    if x.stride(2) != 1 or x.stride(1) != head_dim:
+        raise ValueError("x must be contiguous within a token ([heads, head_dim] row-major)")
+    if tuple(cache.shape[1:]) != (heads, head_dim) or not cache.is_contiguous():
+        raise ValueError("cache must be a contiguous [num_slots, heads, head_dim] uint8 tensor")
+    st = load_library().fp8_kv_append(x.data_ptr(), _dt_of(x), tokens, heads, head_dim, x.stride(0),
+                                      slots.data_ptr(), fmt, scale_kind, scales.data_ptr(), cache.data_ptr(),
+                                      cache.shape[0], _stream(stream))
+    _check("fp8_kv_append", st)
+    return cache
+
+
+def fp8_kv_gather(cache, slots, scales, fmt: int, scale_kind: int, out_dtype: int = DT_BF16, out=None,
+                  stream=None):
+    """Dequantize on read: rows slots (int64 [n]) of cache [num_slots, heads,
+    head_dim] as fp32 or bf16 [n, heads, head_dim] (zeros for slots outside the
+    pool).  Returns out."""
+    torch = _torch()
+    num_slots, heads, head_dim = cache.shape
+    n = slots.shape[0]
+    if out is None:
+        out = torch.empty((n, heads, head_dim), dtype=_torch_dtype(out_dtype), device=cache.device)
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    st = load_library().fp8_kv_gather(cache.data_ptr(), num_slots, heads, head_dim, slots.data_ptr(), n, fmt,
+                                      scale_kind, scales.data_ptr(), out.data_ptr(), _dt_of(out), _stream(stream))
+    _check("fp8_kv_gather", st)
+    return out

@@ -6,6 +6,7 @@
 #include <limits.h>
 
 #include "kernels.h"
+#include "kv_cache.h"
 
 using namespace fp8blk;
 
@@ -40,6 +41,18 @@ fp8_status_t check_operand(int64_t rows, int64_t cols, fp8_granularity_t g) {
 
 fp8_status_t hip_status(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_HIP; }
 
+// Largest KV-cache row (heads * head_dim elements).
+constexpr int64_t kMaxKvRow = int64_t(1) << 24;
+
+bool valid_kv_scale(fp8_kv_scale_t k) { return k >= FP8_KV_SCALE_TENSOR && k <= FP8_KV_SCALE_CHANNEL; }
+
+// Row length L = heads * head_dim of a KV cache, or -1 for an invalid shape.
+int64_t kv_row(int64_t heads, int64_t head_dim) {
+  if (heads < 0 || head_dim < 0 || head_dim % 16 != 0) return -1;
+  if (heads > 0 && head_dim > kMaxKvRow / heads) return -1;
+  return heads * head_dim;
+}
+
 }  // namespace
 
 extern "C" {
@@ -49,7 +62,7 @@ const char* fp8_status_string(fp8_status_t st) {
     case FP8_OK: return "ok";
     case FP8_ERR_NULL: return "a required pointer is NULL";
     case FP8_ERR_ENUM: return "invalid format, granularity, dtype or algorithm value";
-    case FP8_ERR_SHAPE: return "invalid shape (negative, K % 128, rows % 128 for 128x128 blocks, M/N % 16, GEMM K > 2^22, or too large)";
+    case FP8_ERR_SHAPE: return "invalid shape (negative, K % 128, rows % 128 for 128x128 blocks, M/N % 16, GEMM K > 2^22, KV head_dim % 16 or row stride, or too large)";
     case FP8_ERR_UNSUPPORTED: return "unsupported combination";
     case FP8_ERR_WORKSPACE: return "workspace missing or too small";
     case FP8_ERR_HIP: return "HIP launch failed";
@@ -233,6 +246,39 @@ fp8_status_t fp8_gemm_blockscaled(const uint8_t* a, fp8_format_t a_fmt, fp8_gran
                                   void* out, fp8_dtype_t out_dt, hipStream_t stream) {
   return fp8_gemm_blockscaled_ex(a, a_fmt, a_g, a_scales, b, b_fmt, b_g, b_scales, M, N, K, out, out_dt,
                                  FP8_GEMM_AUTO, FP8_ACCUM_FP32, stream);
+}
+
+fp8_status_t fp8_kv_append(const void* x, fp8_dtype_t x_dt, int64_t tokens, int64_t heads, int64_t head_dim,
+                           int64_t ld_x, const int64_t* slots, fp8_format_t fmt, fp8_kv_scale_t scale_kind,
+                           const float* scales, uint8_t* cache, int64_t num_slots, hipStream_t stream) {
+  if (!valid_dt(x_dt) || !valid_fmt(fmt) || !valid_kv_scale(scale_kind)) return FP8_ERR_ENUM;
+  const int64_t L = kv_row(heads, head_dim);
+  if (L < 0 || tokens < 0 || num_slots < 0) return FP8_ERR_SHAPE;
+  if (tokens == 0 || L == 0) return FP8_OK;
+  const int64_t x_elems = mul_checked(tokens, ld_x);
+  if (ld_x < L || x_elems < 0 || x_elems > INT64_MAX / 4 || mul_checked(num_slots, L) < 0) return FP8_ERR_SHAPE;
+  if (!x || !slots || !scales || !cache) return FP8_ERR_NULL;
+  const int64_t esize = x_dt == FP8_DT_BF16 ? 2 : 4;
+  if (!aligned(x, 16) || (ld_x * esize) % 16 != 0 || !aligned(slots, 8) || !aligned(scales, 4) ||
+      !aligned(cache, 16))
+    return FP8_ERR_ALIGN;
+  return hip_status(launch_kv_append(x, (int)x_dt, ld_x, slots, tokens, (int)fmt, (int)scale_kind, scales,
+                                     (int)head_dim, L, cache, num_slots, stream));
+}
+
+fp8_status_t fp8_kv_gather(const uint8_t* cache, int64_t num_slots, int64_t heads, int64_t head_dim,
+                           const int64_t* slots, int64_t n, fp8_format_t fmt, fp8_kv_scale_t scale_kind,
+                           const float* scales, void* out, fp8_dtype_t out_dt, hipStream_t stream) {
+  if (!valid_dt(out_dt) || !valid_fmt(fmt) || !valid_kv_scale(scale_kind)) return FP8_ERR_ENUM;
+  const int64_t L = kv_row(heads, head_dim);
+  if (L < 0 || n < 0 || num_slots < 0) return FP8_ERR_SHAPE;
+  if (n == 0 || L == 0) return FP8_OK;
+  const int64_t out_elems = mul_checked(n, L);
+  if (out_elems < 0 || out_elems > INT64_MAX / 4 || mul_checked(num_slots, L) < 0) return FP8_ERR_SHAPE;
+  if (!slots || !scales || !out || (num_slots > 0 && !cache)) return FP8_ERR_NULL;
+  if (!aligned(cache, 16) || !aligned(slots, 8) || !aligned(scales, 4) || !aligned(out, 16)) return FP8_ERR_ALIGN;
+  return hip_status(launch_kv_gather(cache, num_slots, slots, n, (int)fmt, (int)scale_kind, scales, (int)head_dim, L,
+                                     out, (int)out_dt, stream));
 }
 
 }  // extern "C"

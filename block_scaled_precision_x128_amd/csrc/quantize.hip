@@ -18,6 +18,7 @@
 //   TENSOR      amax partials per workgroup into the workspace, then a second
 //               kernel reduces them and encodes
 #include "device_common.h"
+#include "given_scale.h"
 #include "kernels.h"
 
 namespace fp8blk {
@@ -248,6 +249,7 @@ __global__ __launch_bounds__(256) void k_quant_given_scale(const void* __restric
   } else {
     s = *scale;
   }
+  const GivenScale gs = given_scale(s);
   float m = 0.0f;
   const int64_t G = (int64_t)gridDim.x * 256;
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < nch; idx += 4 * G) {
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(256) void k_quant_given_scale(const void* __restric
       if (idx + u * G < nch) {
         m = fmaxf(m, local_amax<8>(v[u]));
         uint32_t out[2];
-        encode_scaled<FMT, 8>(v[u], s, out);
+        encode_given<FMT, 8>(v[u], gs, out);
         *reinterpret_cast<u32x2*>(q + 8 * (idx + u * G)) = u32x2{out[0], out[1]};
       }
     }

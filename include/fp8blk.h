@@ -107,7 +107,7 @@ typedef enum {
   FP8_ERR_ENUM = 2,        /* a format / granularity / dtype / algo value is invalid */
   FP8_ERR_SHAPE = 3,       /* negative size, K % 128 != 0, rows % 128 != 0 for     */
                            /* 128x128 blocks, M or N % 16 != 0 or K > 2^22 for the  */
-                           /* GEMM                                                  */
+                           /* GEMM, KV head_dim % 16 != 0 or ld_x < heads*head_dim  */
   FP8_ERR_UNSUPPORTED = 4, /* a valid but unsupported combination                 */
   FP8_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required          */
   FP8_ERR_HIP = 6,         /* a HIP launch failed                                  */
@@ -243,6 +243,54 @@ fp8_status_t fp8_gemm_blockscaled_quant(const uint8_t* a, fp8_format_t a_fmt, fp
                                         int64_t M, int64_t N, int64_t K,
                                         fp8_format_t out_fmt, uint8_t* out_codes, float* out_scales,
                                         fp8_accum_t accum, hipStream_t stream);
+
+/* ---- FP8 KV cache ----------------------------------------------------------
+ * Key and value states stored as FP8 codes, one byte per element ("FP8
+ * Mixed-Precision Serving", section "FP8 KV Cache Architecture and Serving
+ * Latency": Memory_KV = 2 * B * L * N_heads * D_head * bytes, halved from bf16;
+ * "FP8 Serving", quality table and "Things to try": per-tensor or per-channel
+ * scales, E5M2 as the wider-range format).
+ * The cache is a pool of num_slots slots; a slot holds one token's
+ * [heads, head_dim] codes (uint8 [num_slots, heads, head_dim], row-major).  A
+ * paged cache with blocks of b tokens is the same pool with slot =
+ * block * b + offset.  Keys and values are two caches and two calls.
+ * Scales are static (calibrated by the caller) fp32 values, positive and not
+ * NaN (+Inf allowed: codes become signed zeros):
+ *   FP8_KV_SCALE_TENSOR   float[1]
+ *   FP8_KV_SCALE_HEAD     float[heads]
+ *   FP8_KV_SCALE_CHANNEL  float[heads * head_dim]   (head-major)
+ * Shapes: head_dim % 16 == 0; heads * head_dim <= 2^24.  Empty calls (no
+ * tokens / rows, or heads * head_dim == 0) are valid and do nothing.
+ * Duplicate append slots in one call race (one of the rows lands). */
+typedef enum {
+  FP8_KV_SCALE_TENSOR = 0,
+  FP8_KV_SCALE_HEAD = 1,
+  FP8_KV_SCALE_CHANNEL = 2
+} fp8_kv_scale_t;
+
+/* Quantize on append: for t in [0, tokens) with 0 <= slots[t] < num_slots,
+ * cache[slots[t]] = code(RN32(x[t] / s)) elementwise, where code() rounds to
+ * nearest even and saturates to +-Vmax (also when the quotient leaves the
+ * fp32 range); tokens whose slot is outside the pool are skipped (padding).
+ *   x      fp32 or bf16 [tokens, ld_x] with row t's [heads, head_dim] values
+ *          in its first heads * head_dim elements; ld_x >= heads * head_dim and
+ *          rows 16-byte aligned (ld_x % 4 == 0 for fp32, % 8 for bf16;
+ *          FP8_ERR_ALIGN otherwise), so x may be a slice of a fused QKV output
+ *   slots  int64 [tokens], device, 8-byte aligned
+ *   cache  uint8 [num_slots, heads, head_dim], 16-byte aligned
+ * x must be finite. */
+fp8_status_t fp8_kv_append(const void* x, fp8_dtype_t x_dt, int64_t tokens, int64_t heads, int64_t head_dim,
+                           int64_t ld_x, const int64_t* slots, fp8_format_t fmt, fp8_kv_scale_t scale_kind,
+                           const float* scales, uint8_t* cache, int64_t num_slots, hipStream_t stream);
+
+/* Dequantize on read: out[i] = RN32(decode(cache[slots[i]]) * s) elementwise,
+ * rounded to bf16 (nearest even) when out_dt is FP8_DT_BF16; a row whose slot
+ * is outside [0, num_slots) is written as zeros.
+ *   slots  int64 [n], device, 8-byte aligned
+ *   out    [n, heads, head_dim] contiguous, 16-byte aligned */
+fp8_status_t fp8_kv_gather(const uint8_t* cache, int64_t num_slots, int64_t heads, int64_t head_dim,
+                           const int64_t* slots, int64_t n, fp8_format_t fmt, fp8_kv_scale_t scale_kind,
+                           const float* scales, void* out, fp8_dtype_t out_dt, hipStream_t stream);
 
 #ifdef __cplusplus
 }

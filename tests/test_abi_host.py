@@ -142,3 +142,48 @@ def test_quantize_delayed_validation(lib):
     assert f(*args(ws=None)) == 5
     assert f(*args(wsb=16)) == 5
     assert f(*args(sc=FAKE + 2)) == 7
+
+
+def test_kv_append_validation(lib):
+    f = lib.fp8_kv_append
+    args = lambda x=FAKE, dt=1, t=4, h=8, d=128, ld=1024, sl=FAKE, fmt=0, sk=0, sc=FAKE, c=FAKE, ns=64: (
+        x, dt, t, h, d, ld, sl, fmt, sk, sc, c, ns, None)
+    assert f(*args(dt=2)) == 2
+    assert f(*args(fmt=2)) == 2
+    assert f(*args(sk=3)) == 2
+    assert f(*args(d=120)) == 3               # head_dim % 16
+    assert f(*args(h=-1)) == 3
+    assert f(*args(ns=-1)) == 3
+    assert f(*args(ld=1000)) == 3             # stride shorter than a row
+    assert f(*args(h=1 << 20, d=1 << 10)) == 3  # row over 2^24 elements
+    assert f(*args(t=1 << 62)) == 3           # x size overflows
+    assert f(*args(x=None)) == 1
+    assert f(*args(sl=None)) == 1
+    assert f(*args(sc=None)) == 1
+    assert f(*args(c=None)) == 1
+    assert f(*args(ld=1028)) == 7             # bf16 rows not 16-byte aligned
+    assert f(*args(x=FAKE + 8)) == 7
+    assert f(*args(sl=FAKE + 4)) == 7
+    assert f(*args(sc=FAKE + 2)) == 7
+    assert f(*args(c=FAKE + 8)) == 7
+    # nothing to do: no launch, OK even with null pointers
+    assert f(*args(t=0, x=None, sl=None, c=None)) == 0
+    assert f(*args(h=0, x=None, sl=None, c=None)) == 0
+
+
+def test_kv_gather_validation(lib):
+    f = lib.fp8_kv_gather
+    args = lambda c=FAKE, ns=64, h=8, d=128, sl=FAKE, n=4, fmt=1, sk=2, sc=FAKE, o=FAKE, odt=1: (
+        c, ns, h, d, sl, n, fmt, sk, sc, o, odt, None)
+    assert f(*args(odt=5)) == 2
+    assert f(*args(sk=-1)) == 2
+    assert f(*args(d=8)) == 3
+    assert f(*args(n=-2)) == 3
+    assert f(*args(n=1 << 62)) == 3
+    assert f(*args(sl=None)) == 1
+    assert f(*args(sc=None)) == 1
+    assert f(*args(o=None)) == 1
+    assert f(*args(c=None)) == 1
+    assert f(*args(o=FAKE + 4)) == 7
+    assert f(*args(c=FAKE + 1)) == 7
+    assert f(*args(n=0, sl=None, o=None)) == 0

@@ -42,3 +42,25 @@ def test_delayed_scaling_sequence(fmt, dt, margin):
         assert host(s).view(np.uint32)[0] == np.float32(want_s).view(np.uint32), (label, host(s), want_s)
         assert_codes_equal(host(q), want_q, label + " codes", x32)
         assert np.array_equal(host(hist_d).view(np.uint32), hist_o.view(np.uint32)), (label, host(hist_d), hist_o)
+
+
+@pytest.mark.parametrize("fmt", [fb.E4M3, fb.E5M2])
+def test_delayed_scale_far_from_the_data(fmt):
+    """A history far below the data (quotients beyond the fp32 range: codes
+    saturate, E5M2 never gives Inf) and a history whose scale overflows fp32
+    (scale +Inf: codes are signed zeros)."""
+    cases = [("tiny history", np.array([1e-30, 0.0], np.float32), 0),
+             ("scale overflows", np.array([3e38, 1.0], np.float32), 31)]
+    rng = np.random.default_rng(55 + fmt)
+    for name, hist, margin in cases:
+        x = (rng.standard_normal((8, 128)) * 10).astype(np.float32)
+        x[0, :4] = [1e30, -1e30, 0.0, -0.0]
+        label = f"delayed extreme fmt={fmt} {name}"
+        say(label)
+        hist_d = dev(hist.copy())
+        q, s = fb.fp8_quantize_delayed(dev(x), fmt, hist_d, 1, margin)
+        torch.cuda.synchronize()
+        want_q, want_s, want_h = quant.quantize_delayed(x, hist, 1, margin, fmt)
+        assert host(s).view(np.uint32)[0] == np.float32(want_s).view(np.uint32), (label, host(s), want_s)
+        assert_codes_equal(host(q), want_q, label + " codes", x)
+        assert np.array_equal(host(hist_d).view(np.uint32), want_h.view(np.uint32)), label

@@ -13,6 +13,11 @@ paragraph after the qdq listing), weights "tightly clustered around zero"
 orders of magnitude for the E5M2 operand (page "The FP8 Family", E5M2 row of
 the format table).
 
+The FP8 KV-cache workload (KV_CONFIGS) follows page "FP8 Serving" (memory
+table row "KV cache (8k, batch 32)" for an 8B model; keys and values carry
+channel-structured outliers) with the published Llama 3.1 8B attention shape:
+8 KV heads of 128.
+
 Generator recipe (fixed):
   rng = numpy.random.default_rng(seed)            # PCG64
   X   = rng.standard_normal((M, K), float32)
@@ -20,6 +25,17 @@ Generator recipe (fixed):
   W   = rng.standard_normal((N, K), float32) * 0.02      (normal weights)
      or sign * 10**rng.uniform(-6, 3, (N, K))            (log-uniform, E5M2)
   bf16 inputs are the fp32 draws rounded to bf16 (round to nearest even).
+KV cache:
+  channels with outliers: rng.choice(heads * head_dim, n, replace=False) from
+  default_rng(seed); sigma = factor there, 1 elsewhere
+  values  = rng.standard_normal((tokens, heads, head_dim), float32) * sigma
+  slots   = paged: blocks of `block` tokens, a pool of ceil(capacity * tokens /
+            block) blocks, sequence blocks = a random permutation of the pool
+            (default_rng(seed + 1)); token t of sequence b sits in slot
+            perm[b * blocks_per_seq + t // block] * block + t % block
+  static scales (given, as a calibration would): sigma / 56 per channel, the
+            channel sigma's maximum / 56 per head and per tensor (8 sigma at
+            the top of the E4M3 range, 448 = 8 * 56)
 """
 
 from __future__ import annotations
@@ -33,6 +49,7 @@ import numpy as np
 E4M3, E5M2 = 0, 1
 GRAN_TENSOR, GRAN_ROW, GRAN_TILE_1x128, GRAN_BLOCK_128x128, GRAN_MX32 = 0, 1, 2, 3, 4
 DT_F32, DT_BF16 = 0, 1
+KV_SCALE_TENSOR, KV_SCALE_HEAD, KV_SCALE_CHANNEL = 0, 1, 2
 
 
 @dataclasses.dataclass(frozen=True)
@@ -152,3 +169,88 @@ def storage_to_f32(a: np.ndarray, dtype: int) -> np.ndarray:
     if dtype == DT_BF16:
         return bf16_bits_to_f32(a)
     return np.asarray(a, dtype=np.float32)
+
+
+# ---- FP8 KV cache --------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class KvWorkload:
+    name: str
+    seed: int
+    batch: int
+    context: int           # tokens per sequence
+    heads: int             # KV heads
+    head_dim: int
+    block: int             # paged-cache block, tokens
+    capacity: float        # pool slots / tokens held
+    fmt: int
+    scale_kind: int
+    in_dtype: int
+    out_dtype: int
+    outlier_frac: float    # fraction of channels with outliers
+    outlier_factor: float  # their sigma
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.context
+
+    @property
+    def row(self) -> int:
+        return self.heads * self.head_dim
+
+    @property
+    def blocks_per_seq(self) -> int:
+        return -(-self.context // self.block)
+
+
+KV_CONFIGS = {
+    "kv_llama8b_b32_ctx8k": KvWorkload(
+        "kv_llama8b_b32_ctx8k", 201, 32, 8192, 8, 128, 16, 1.25, E4M3, KV_SCALE_CHANNEL, DT_BF16, DT_BF16,
+        1.0 / 64, 20.0),
+}
+
+
+def kv_sigma(wl: KvWorkload) -> np.ndarray:
+    """Per-channel standard deviation [heads, head_dim]."""
+    rng = np.random.default_rng(wl.seed)
+    sig = np.ones(wl.row, np.float32)
+    n = int(round(wl.outlier_frac * wl.row))
+    if n > 0:
+        sig[rng.choice(wl.row, n, replace=False)] = np.float32(wl.outlier_factor)
+    return sig.reshape(wl.heads, wl.head_dim)
+
+
+def draw_kv(wl: KvWorkload, tokens: int, rng: np.random.Generator) -> np.ndarray:
+    """Key or value states [tokens, heads, head_dim] as fp32 values."""
+    return rng.standard_normal((tokens, wl.heads, wl.head_dim), dtype=np.float32) * kv_sigma(wl)[None]
+
+
+def kv_slots(wl: KvWorkload, batch: Optional[int] = None, context: Optional[int] = None) -> np.ndarray:
+    """Slot of every token, sequence-major ([batch * context] int64), for a
+    paged pool whose blocks are handed out in a random order."""
+    batch = wl.batch if batch is None else batch
+    context = wl.context if context is None else context
+    bps = -(-context // wl.block)
+    pool = max(int(np.ceil(wl.capacity * batch * bps)), batch * bps)
+    perm = np.random.default_rng(wl.seed + 1).permutation(pool)[: batch * bps].reshape(batch, bps)
+    t = np.arange(context)
+    slots = perm[:, t // wl.block] * wl.block + (t % wl.block)[None, :]
+    return slots.reshape(-1).astype(np.int64)
+
+
+def kv_pool_slots(wl: KvWorkload, batch: Optional[int] = None, context: Optional[int] = None) -> int:
+    batch = wl.batch if batch is None else batch
+    context = wl.context if context is None else context
+    bps = -(-context // wl.block)
+    return max(int(np.ceil(wl.capacity * batch * bps)), batch * bps) * wl.block
+
+
+def kv_scales(wl: KvWorkload, scale_kind: Optional[int] = None) -> np.ndarray:
+    """Static scales of the given kind (float32 [1], [heads] or [heads * head_dim])."""
+    kind = wl.scale_kind if scale_kind is None else scale_kind
+    sig = kv_sigma(wl)
+    if kind == KV_SCALE_CHANNEL:
+        return (sig / np.float32(56.0)).reshape(-1).astype(np.float32)
+    if kind == KV_SCALE_HEAD:
+        return (sig.max(axis=1) / np.float32(56.0)).astype(np.float32)
+    return np.array([sig.max() / np.float32(56.0)], np.float32)
