@@ -6,13 +6,19 @@
 // channel-structured outliers, E5M2 for range.)
 //
 // The cache is a pool of slots, each one token's L = heads * head_dim codes.
-// Thread (row, c) handles elements [16c, 16c + 16) of a row: one 16-byte code
-// access, inside one head since head_dim % 16 == 0.  A thread keeps its c for
-// all of its rows (rows advance by a fixed row step), so per-head and
-// per-channel scales, and the division constants of the append, are loaded
-// and prepared once per thread rather than per element.  Both kernels are
-// pure streams: 1 code byte plus 2 (bf16) or 4 (fp32) bytes of values per
-// element, and 8 bytes of slot index per row.
+// A thread owns 16 elements of a row for all of the rows it visits (rows
+// advance by a fixed row step), so per-head and per-channel scales, and the
+// division constants of the append, are loaded and prepared once per thread
+// rather than per element.  Both kernels are pure streams: 1 code byte plus 2
+// (bf16) or 4 (fp32) bytes of values per element, and 8 bytes of slot index
+// per row.
+//   append: thread c owns elements [16c, 16c + 16): its 16 code bytes are one
+//           store, and the stores of a wave cover a contiguous 1 KB.
+//   read:   the 16 elements are P pieces of 16/P, at elements (16/P)(c + p L/16)
+//           for p < P, so that every 16-byte store of the output (8 bf16 or 4
+//           fp32 values) is contiguous across the wave.  Stores at a 32-byte
+//           lane stride (16 contiguous elements per thread) measured 15-20%
+//           slower on this write-heavy stream.
 #include "device_common.h"
 #include "gemm_common.h"  // num_cus()
 #include "given_scale.h"
@@ -95,67 +101,101 @@ __global__ __launch_bounds__(256) void k_kv_append(const void* __restrict__ x, i
 }
 
 // out[r] = RN32(decode(cache[slots[r]]) * s), then bf16 (nearest even) when
-// ODT is bf16; zeros for a slot outside the pool.  out is [rows, L].
+// ODT is bf16; zeros for a slot outside the pool.  out is [rows, L].  Two rows
+// per iteration: both slot loads, then both rows' code loads, are in flight
+// together.
 template <int FMT, int SK, int ODT>
 __global__ __launch_bounds__(256) void k_kv_gather(const uint8_t* __restrict__ cache,
                                                     const int64_t* __restrict__ slots,
                                                     const float* __restrict__ scales, KvShape sh,
                                                     void* __restrict__ out) {
+  constexpr int P = ODT == DT_F32 ? 4 : 2;   // pieces per thread
+  constexpr int E = 16 / P;                  // elements per piece: one 16-byte output store
+  constexpr int U = 2;                       // rows per iteration
   const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   int64_t r = tid / sh.cpr;
   if (r >= sh.row_step) return;
-  const int e0 = 16 * (int)(tid - r * sh.cpr);
+  const int c = (int)(tid - r * sh.cpr);
   const int64_t L = (int64_t)sh.cpr * 16;
-  constexpr int NS = SK == KV_CHANNEL ? 16 : 1;
+  int ep[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) ep[p] = E * (c + p * sh.cpr);
+  constexpr int NS = SK == KV_CHANNEL ? 16 : (SK == KV_HEAD ? P : 1);
   float s[NS];
-  if constexpr (SK == KV_TENSOR) {
-    s[0] = scales[0];
-  } else if constexpr (SK == KV_HEAD) {
-    s[0] = scales[e0 / sh.head_dim];
-  } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = scales[e0 + i];
-  }
-  for (; r < sh.rows; r += sh.row_step) {
-    const int64_t slot = slots[r];
-    float v[16];
-    if ((uint64_t)slot < (uint64_t)sh.num_slots) {
-      const u32x4 q = *reinterpret_cast<const u32x4*>(cache + slot * L + e0);
-      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  for (int p = 0; p < P; ++p) {
+    if constexpr (SK == KV_CHANNEL) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const v2f lo = decode2<FMT>(w[i], false), hi = decode2<FMT>(w[i], true);
-        v[4 * i] = lo.x; v[4 * i + 1] = lo.y; v[4 * i + 2] = hi.x; v[4 * i + 3] = hi.y;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] *= s[NS == 16 ? i : 0];
+      for (int i = 0; i < E; ++i) s[p * E + i] = scales[ep[p] + i];
+    } else if constexpr (SK == KV_HEAD) {
+      s[p] = scales[ep[p] / sh.head_dim];
     } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+      if (p == 0) s[0] = scales[0];
     }
-    if constexpr (ODT == DT_F32) {
-      float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + r * L + e0);
+  }
+  for (; r < sh.rows; r += U * sh.row_step) {
+    int64_t slot[U];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-    } else {
-      u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + r * L + e0);
+    for (int u = 0; u < U; ++u) {
+      const int64_t rr = r + u * sh.row_step;
+      slot[u] = rr < sh.rows ? slots[rr] : -1;
+    }
+    uint32_t w[U][P][E / 4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        dst[i] = u32x4{kv_pack_bf16(v[8 * i], v[8 * i + 1]), kv_pack_bf16(v[8 * i + 2], v[8 * i + 3]),
-                       kv_pack_bf16(v[8 * i + 4], v[8 * i + 5]), kv_pack_bf16(v[8 * i + 6], v[8 * i + 7])};
+    for (int u = 0; u < U; ++u) {
+      const bool ok = (uint64_t)slot[u] < (uint64_t)sh.num_slots;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        if constexpr (E == 8) {
+          const u32x2 q = ok ? *reinterpret_cast<const u32x2*>(cache + slot[u] * L + ep[p]) : u32x2{0, 0};
+          w[u][p][0] = q.x;
+          w[u][p][1] = q.y;
+        } else {
+          w[u][p][0] = ok ? *reinterpret_cast<const uint32_t*>(cache + slot[u] * L + ep[p]) : 0u;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t rr = r + u * sh.row_step;
+      if (rr >= sh.rows) break;
+      const bool ok = (uint64_t)slot[u] < (uint64_t)sh.num_slots;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        float v[E];
+#pragma unroll
+        for (int i = 0; i < E / 4; ++i) {
+          const v2f lo = decode2<FMT>(w[u][p][i], false), hi = decode2<FMT>(w[u][p][i], true);
+          v[4 * i] = lo.x; v[4 * i + 1] = lo.y; v[4 * i + 2] = hi.x; v[4 * i + 3] = hi.y;
+        }
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const float si = s[SK == KV_CHANNEL ? p * E + i : (SK == KV_HEAD ? p : 0)];
+          v[i] = ok ? v[i] * si : 0.0f;
+        }
+        if constexpr (ODT == DT_F32) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + rr * L + ep[p]) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + rr * L + ep[p]) =
+              u32x4{kv_pack_bf16(v[0], v[1]), kv_pack_bf16(v[2], v[3]), kv_pack_bf16(v[4], v[5]),
+                    kv_pack_bf16(v[6], v[7])};
+        }
+      }
     }
   }
 }
 
-// Rows in flight: enough threads for full occupancy (8 workgroups of 256 per
-// CU), but no more rows than there are.
+// Rows in flight: threads for 4 workgroups of 256 per CU (measured: more
+// waves per CU slow these write-carrying streams down, fewer leave reads
+// short of requests), but no more rows than there are.
 static KvShape kv_shape(int64_t rows, int64_t num_slots, int64_t L, int head_dim) {
   KvShape sh;
   sh.rows = rows;
   sh.num_slots = num_slots;
   sh.cpr = (int)(L / 16);
   sh.head_dim = head_dim;
-  const int64_t target = (int64_t)num_cus() * 8 * 256;
+  const int64_t target = (int64_t)num_cus() * 4 * 256;
   const int64_t rs = (target + sh.cpr - 1) / sh.cpr;
   sh.row_step = rows < rs ? rows : rs;
   return sh;
