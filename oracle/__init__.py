@@ -12,6 +12,9 @@ Contents
               dequantize, delayed scaling, and the FP8 KV-cache codec
               (quantize on append, dequantize on read, static scales per
               tensor / head / channel)
+  fp4      -- E2M1 (FP4) with MXFP4 (32-element UE8M0) and NVFP4 (16-element
+              E4M3 microscale + fp32 tensor scale) quantize, dequantize and the
+              GEMM reference
   gemm     -- exact (fp64) GEMM on the dequantized operands, |x|.|w| bound and the
               elementwise tolerance test
 
