@@ -14,6 +14,7 @@ Enum values (same as the C header):
   GEMM kernels   GEMM_AUTO = 0, GEMM_TILED = 1, GEMM_SKINNY = 2
   accumulation   ACCUM_FP32 = 0 (exact products, fp32 sums), ACCUM_NATIVE = 1
   KV scales      KV_SCALE_TENSOR = 0, KV_SCALE_HEAD = 1, KV_SCALE_CHANNEL = 2
+  FP4 scaling    FP4_MX = 0 (32-element UE8M0), FP4_NV = 1 (16-element E4M3 + fp32 tensor)
 """
 
 from __future__ import annotations
@@ -28,6 +29,7 @@ DT_F32, DT_BF16 = 0, 1
 GEMM_AUTO, GEMM_TILED, GEMM_SKINNY = 0, 1, 2
 ACCUM_FP32, ACCUM_NATIVE = 0, 1
 KV_SCALE_TENSOR, KV_SCALE_HEAD, KV_SCALE_CHANNEL = 0, 1, 2
+FP4_MX, FP4_NV = 0, 1
 
 FP8_OK = 0
 STATUS_NAMES = {0: "FP8_OK", 1: "FP8_ERR_NULL", 2: "FP8_ERR_ENUM", 3: "FP8_ERR_SHAPE",
@@ -66,6 +68,11 @@ _SIGS = {
                                  _c.c_void_p]),
     "fp8_kv_gather": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_int64,
                                  _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p]),
+    "fp4_quantize_workspace_bytes": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int]),
+    "fp4_quantize": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p,
+                                _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "fp4_dequantize": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int,
+                                  _c.c_void_p, _c.c_int, _c.c_void_p]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -290,3 +297,46 @@ def fp8_kv_gather(cache, slots, scales, fmt: int, scale_kind: int, out_dtype: in
                                       scale_kind, scales.data_ptr(), out.data_ptr(), _dt_of(out), _stream(stream))
     _check("fp8_kv_gather", st)
     return out
+
+
+def fp4_block(kind: int) -> int:
+    return 32 if kind == FP4_MX else 16
+
+
+def fp4_quantize_workspace_bytes(rows: int, cols: int, kind: int) -> int:
+    return int(load_library().fp4_quantize_workspace_bytes(rows, cols, kind))
+
+
+def fp4_quantize(x, kind: int, q=None, block_scales=None, tensor_scale=None, workspace=None, stream=None):
+    """Quantize x [rows, cols] to packed E2M1 codes.  Returns (q [rows, cols/2]
+    uint8, block_scales uint8 [rows, cols/32 or cols/16], tensor_scale float32
+    [1] or None for MX)."""
+    torch = _torch()
+    rows, cols = x.shape
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if block_scales is None:
+        block_scales = torch.empty((rows, cols // fp4_block(kind)), dtype=torch.uint8, device=dev)
+    if kind == FP4_NV and tensor_scale is None:
+        tensor_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    wsb = fp4_quantize_workspace_bytes(rows, cols, kind)
+    if workspace is None and wsb:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st = load_library().fp4_quantize(x.data_ptr(), _dt_of(x), rows, cols, kind, q.data_ptr(),
+                                     block_scales.data_ptr(), _ptr(tensor_scale), _ptr(workspace),
+                                     workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check("fp4_quantize", st)
+    return q, block_scales, tensor_scale
+
+
+def fp4_dequantize(q, block_scales, tensor_scale, kind: int, out_dtype: int = DT_F32, y=None, stream=None):
+    """Dequantize packed E2M1 codes [rows, cols/2] to fp32 or bf16 [rows, cols]."""
+    torch = _torch()
+    rows, half = q.shape
+    if y is None:
+        y = torch.empty((rows, 2 * half), dtype=_torch_dtype(out_dtype), device=q.device)
+    st = load_library().fp4_dequantize(q.data_ptr(), block_scales.data_ptr(), _ptr(tensor_scale), rows, 2 * half,
+                                       kind, y.data_ptr(), _dt_of(y), _stream(stream))
+    _check("fp4_dequantize", st)
+    return y

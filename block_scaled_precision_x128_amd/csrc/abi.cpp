@@ -5,6 +5,7 @@
 
 #include <limits.h>
 
+#include "fp4.h"
 #include "kernels.h"
 #include "kv_cache.h"
 
@@ -43,6 +44,8 @@ fp8_status_t hip_status(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ER
 
 // Largest KV-cache row (heads * head_dim elements).
 constexpr int64_t kMaxKvRow = int64_t(1) << 24;
+
+bool valid_fp4(fp4_scaling_t k) { return k == FP4_SCALE_MX || k == FP4_SCALE_NV; }
 
 bool valid_kv_scale(fp8_kv_scale_t k) { return k >= FP8_KV_SCALE_TENSOR && k <= FP8_KV_SCALE_CHANNEL; }
 
@@ -144,7 +147,7 @@ namespace {
 
 // Validation and mode selection shared by the GEMM entry points; fills p
 // (without the output) and the scale mode.  Returns FP8_OK or an error.
-fp8_status_t gemm_common(const uint8_t* a, fp8_format_t a_fmt, fp8_granularity_t a_g, const void* a_scales,
+static fp8_status_t gemm_common(const uint8_t* a, fp8_format_t a_fmt, fp8_granularity_t a_g, const void* a_scales,
                          const uint8_t* b, fp8_format_t b_fmt, fp8_granularity_t b_g, const void* b_scales,
                          int64_t M, int64_t N, int64_t K, fp8_accum_t accum, GemmArgs& p, int& mode) {
   if (!valid_fmt(a_fmt) || !valid_fmt(b_fmt) || !valid_gran(a_g) || !valid_gran(b_g)) return FP8_ERR_ENUM;
@@ -174,7 +177,7 @@ fp8_status_t gemm_common(const uint8_t* a, fp8_format_t a_fmt, fp8_granularity_t
   return FP8_OK;
 }
 
-fp8_status_t check_operands(const GemmArgs& p) {
+static fp8_status_t check_operands(const GemmArgs& p) {
   if (!p.a || !p.b || !p.sa || !p.sb) return FP8_ERR_NULL;
   if (!aligned(p.a, 16) || !aligned(p.b, 16)) return FP8_ERR_ALIGN;
   // fp32 scales are read as floats; UE8M0 scales as 4-byte words (4 blocks of 32)
@@ -279,6 +282,51 @@ fp8_status_t fp8_kv_gather(const uint8_t* cache, int64_t num_slots, int64_t head
   if (!aligned(cache, 16) || !aligned(slots, 8) || !aligned(scales, 4) || !aligned(out, 16)) return FP8_ERR_ALIGN;
   return hip_status(launch_kv_gather(cache, num_slots, slots, n, (int)fmt, (int)scale_kind, scales, (int)head_dim, L,
                                      out, (int)out_dt, stream));
+}
+
+size_t fp4_quantize_workspace_bytes(int64_t rows, int64_t cols, fp4_scaling_t kind) {
+  if (!valid_fp4(kind) || check_operand(rows, cols, FP8_GRAN_ROW) != FP8_OK) return 0;
+  return kind == FP4_SCALE_NV ? sizeof(float) * (size_t)kFp4Partials : 0;
+}
+
+fp8_status_t fp4_quantize(const void* x, fp8_dtype_t x_dt, int64_t rows, int64_t cols, fp4_scaling_t kind,
+                          uint8_t* q, uint8_t* block_scales, float* tensor_scale, void* workspace, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (!valid_dt(x_dt) || !valid_fp4(kind)) return FP8_ERR_ENUM;
+  const fp8_status_t sh = check_operand(rows, cols, FP8_GRAN_ROW);
+  if (sh != FP8_OK) return sh;
+  const int64_t total = rows * cols;
+  if (kind == FP4_SCALE_NV) {
+    if (!tensor_scale) return FP8_ERR_NULL;
+    if (!aligned(tensor_scale, 4)) return FP8_ERR_ALIGN;
+  }
+  if (total == 0) {
+    if (kind == FP4_SCALE_MX) return FP8_OK;
+    return hip_status(launch_fp4_quantize(x, (int)x_dt, rows, cols, (int)kind, q, block_scales, tensor_scale,
+                                          nullptr, stream));
+  }
+  if (!x || !q || !block_scales) return FP8_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16)) return FP8_ERR_ALIGN;
+  if (kind == FP4_SCALE_NV) {
+    if (!workspace || ws_bytes < sizeof(float) * (size_t)kFp4Partials) return FP8_ERR_WORKSPACE;
+    if (!aligned(workspace, 4)) return FP8_ERR_ALIGN;
+  }
+  return hip_status(launch_fp4_quantize(x, (int)x_dt, rows, cols, (int)kind, q, block_scales, tensor_scale,
+                                        static_cast<float*>(workspace), stream));
+}
+
+fp8_status_t fp4_dequantize(const uint8_t* q, const uint8_t* block_scales, const float* tensor_scale,
+                            int64_t rows, int64_t cols, fp4_scaling_t kind, void* y, fp8_dtype_t y_dt,
+                            hipStream_t stream) {
+  if (!valid_dt(y_dt) || !valid_fp4(kind)) return FP8_ERR_ENUM;
+  const fp8_status_t sh = check_operand(rows, cols, FP8_GRAN_ROW);
+  if (sh != FP8_OK) return sh;
+  if (rows * cols == 0) return FP8_OK;
+  if (!q || !block_scales || !y || (kind == FP4_SCALE_NV && !tensor_scale)) return FP8_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(y, 16) || (kind == FP4_SCALE_NV && !aligned(tensor_scale, 4)))
+    return FP8_ERR_ALIGN;
+  return hip_status(launch_fp4_dequantize(q, block_scales, tensor_scale, rows, cols, (int)kind, y, (int)y_dt,
+                                          stream));
 }
 
 }  // extern "C"

@@ -292,6 +292,44 @@ fp8_status_t fp8_kv_gather(const uint8_t* cache, int64_t num_slots, int64_t head
                            const int64_t* slots, int64_t n, fp8_format_t fmt, fp8_kv_scale_t scale_kind,
                            const float* scales, void* out, fp8_dtype_t out_dt, hipStream_t stream);
 
+/* ---- FP4 (E2M1) with two-level microscaling ---------------------------------
+ * ("Illustrated GPU kernels, Part 8", section "Low precision: FP8, FP4, and
+ * microscaling": the OCP MX block of 32 elements with one UE8M0 scale, and
+ * NVFP4's blocks of 16 with an E4M3 microscale plus one FP32 scale per tensor
+ * that keeps the microscales inside E4M3's range.)
+ * E2M1: 1 sign, 2 exponent, 1 mantissa bit, bias 1; magnitudes 0, 0.5, 1,
+ * 1.5, 2, 3, 4, 6; no Inf or NaN.  Codes are packed two per byte, element 2i
+ * in the low nibble: a [rows, cols] operand is uint8 [rows, cols/2].
+ *   FP4_SCALE_MX  block_scales uint8 [rows, cols/32]: byte e + 127, e the
+ *                 smallest integer with amax <= 6 * 2^e (clamped to
+ *                 [-127, 127]); codes = cast(x * 2^-e).  No tensor scale.
+ *   FP4_SCALE_NV  block_scales uint8 [rows, cols/16]: E4M3 microscale codes;
+ *                 tensor_scale float[1].  s_t = RN32(amax / 2688) (1 when 0);
+ *                 per block u = RN32(amax_b / RN32(6 s_t)), m = E4M3(u) (RNE,
+ *                 saturating), S = RN32(m * s_t); codes = cast(RN32(x / S)),
+ *                 signed zeros when S == 0.
+ * cast() rounds to nearest even, saturates to +-6 and keeps the sign of zero. */
+typedef enum { FP4_SCALE_MX = 0, FP4_SCALE_NV = 1 } fp4_scaling_t;
+
+/* Device workspace fp4_quantize needs (NV: partial maxima of the tensor amax,
+ * at most 32 KiB; MX: 0).  Returns 0 for invalid arguments. */
+size_t fp4_quantize_workspace_bytes(int64_t rows, int64_t cols, fp4_scaling_t kind);
+
+/* Quantize x [rows, cols] (fp32 or bf16, finite) to packed E2M1 codes q with
+ * the block scales (and, for NV, the tensor scale) above.  cols % 128 == 0;
+ * x and q 16-byte aligned, tensor_scale 4-byte aligned.  An empty NV tensor
+ * writes the tensor scale 1. */
+fp8_status_t fp4_quantize(const void* x, fp8_dtype_t x_dt, int64_t rows, int64_t cols, fp4_scaling_t kind,
+                          uint8_t* q, uint8_t* block_scales, float* tensor_scale, void* workspace, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Dequantize: MX y = decode(q) * 2^e (scale byte 255 gives NaN); NV
+ * y = RN32(decode(q) * S), S = RN32(m * s_t); then RNE bf16 when y_dt is
+ * FP8_DT_BF16.  Shapes and alignment as for fp4_quantize. */
+fp8_status_t fp4_dequantize(const uint8_t* q, const uint8_t* block_scales, const float* tensor_scale,
+                            int64_t rows, int64_t cols, fp4_scaling_t kind, void* y, fp8_dtype_t y_dt,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -141,10 +141,14 @@ def quantize_mx(x: np.ndarray):
 
 
 def dequantize_mx(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """decode(q) * 2^e; a scale byte of 255 (never written) reads as NaN, as for
+    the FP8 MX32 scale."""
     q = unpack(packed)
     rows, K = q.shape
-    e = np.asarray(scales, dtype=np.int64) - 127
+    b = np.asarray(scales, dtype=np.int64)
+    e = np.minimum(b, 254) - 127
     v = e2m1_decode(q).reshape(rows, K // MX_BLOCK, MX_BLOCK) * np.ldexp(1.0, e)[..., None]
+    v = np.where((b == 255)[..., None], np.nan, v)
     with np.errstate(over="ignore"):
         return v.reshape(rows, K).astype(np.float32)
 

@@ -23,7 +23,7 @@ def _ensure_built():
 def header_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**(fp8_\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**(fp[48]_\w+)\s*\(", src, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -187,3 +187,42 @@ def test_kv_gather_validation(lib):
     assert f(*args(o=FAKE + 4)) == 7
     assert f(*args(c=FAKE + 1)) == 7
     assert f(*args(n=0, sl=None, o=None)) == 0
+
+
+def test_fp4_validation(lib):
+    f = lib.fp4_quantize
+    args = lambda x=FAKE, dt=1, rows=4, cols=256, kind=1, q=FAKE, bs=FAKE, ts=FAKE, ws=FAKE, wsb=32768: (
+        x, dt, rows, cols, kind, q, bs, ts, ws, wsb, None)
+    assert lib.fp4_quantize_workspace_bytes(4, 256, 1) == 32768
+    assert lib.fp4_quantize_workspace_bytes(4, 256, 0) == 0
+    assert lib.fp4_quantize_workspace_bytes(4, 250, 1) == 0
+    assert f(*args(kind=2)) == 2
+    assert f(*args(dt=3)) == 2
+    assert f(*args(cols=200)) == 3
+    assert f(*args(x=None)) == 1
+    assert f(*args(bs=None)) == 1
+    assert f(*args(ts=None)) == 1            # NV needs the tensor scale
+    assert f(*args(ws=None)) == 5
+    assert f(*args(wsb=100)) == 5
+    assert f(*args(q=FAKE + 4)) == 7
+    assert f(*args(ts=FAKE + 1)) == 7
+    assert f(*args(kind=0, ts=None, ws=None, wsb=0, rows=0)) == 0   # empty MX: nothing to do
+    d = lib.fp4_dequantize
+    dargs = lambda q=FAKE, bs=FAKE, ts=FAKE, rows=4, cols=256, kind=1, y=FAKE, dt=0: (q, bs, ts, rows, cols, kind, y, dt, None)
+    assert d(*dargs(kind=5)) == 2
+    assert d(*dargs(cols=100)) == 3
+    assert d(*dargs(ts=None)) == 1
+    assert d(*dargs(y=FAKE + 8)) == 7
+    assert d(*dargs(rows=0, q=None, y=None)) == 0
+
+
+def test_library_exports_nothing_else(lib):
+    """The C symbols the library exports are exactly the header's functions."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", fb.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    c_syms = sorted(l.split()[-1] for l in out.splitlines() if " T " in l and not l.split()[-1].startswith("_Z"))
+    assert c_syms == header_functions()
