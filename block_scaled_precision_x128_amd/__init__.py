@@ -73,6 +73,9 @@ _SIGS = {
                                 _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "fp4_dequantize": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int,
                                   _c.c_void_p, _c.c_int, _c.c_void_p]),
+    "fp4_gemm_blockscaled": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
+                                        _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p,
+                                        _c.c_int, _c.c_void_p]),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -340,3 +343,20 @@ def fp4_dequantize(q, block_scales, tensor_scale, kind: int, out_dtype: int = DT
                                        kind, y.data_ptr(), _dt_of(y), _stream(stream))
     _check("fp4_dequantize", st)
     return y
+
+
+def fp4_gemm_blockscaled(a, a_scales, a_tensor_scale, b, b_scales, b_tensor_scale, kind: int,
+                         out_dtype: int = DT_F32, out=None, stream=None):
+    """FP4 block-scaled GEMM of packed E2M1 operands a [M, K/2], b [N, K/2]
+    (K-contiguous) with their block (and, NV, tensor) scales.  Returns out
+    [M, N]."""
+    torch = _torch()
+    M, half = a.shape
+    N = b.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=_torch_dtype(out_dtype), device=a.device)
+    st = load_library().fp4_gemm_blockscaled(a.data_ptr(), a_scales.data_ptr(), _ptr(a_tensor_scale), b.data_ptr(),
+                                             b_scales.data_ptr(), _ptr(b_tensor_scale), M, N, 2 * half, kind,
+                                             out.data_ptr(), _dt_of(out), _stream(stream))
+    _check("fp4_gemm_blockscaled", st)
+    return out

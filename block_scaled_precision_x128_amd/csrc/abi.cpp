@@ -329,4 +329,36 @@ fp8_status_t fp4_dequantize(const uint8_t* q, const uint8_t* block_scales, const
                                           stream));
 }
 
+fp8_status_t fp4_gemm_blockscaled(const uint8_t* a, const uint8_t* a_scales, const float* a_tensor_scale,
+                                  const uint8_t* b, const uint8_t* b_scales, const float* b_tensor_scale,
+                                  int64_t M, int64_t N, int64_t K, fp4_scaling_t kind, void* out,
+                                  fp8_dtype_t out_dt, hipStream_t stream) {
+  if (!valid_fp4(kind) || !valid_dt(out_dt)) return FP8_ERR_ENUM;
+  if (M < 0 || N < 0 || K < 0 || M % 16 != 0 || N % 16 != 0 || K % 256 != 0 || K > kMaxGemmK) return FP8_ERR_SHAPE;
+  if (mul_checked(M, N) < 0 || mul_checked(M, K) < 0 || mul_checked(N, K) < 0) return FP8_ERR_SHAPE;
+  if ((M / 128 + 1) * (N / 128 + 1) >= INT_MAX) return FP8_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8_OK;
+  if (!out) return FP8_ERR_NULL;
+  if (!aligned(out, 16)) return FP8_ERR_ALIGN;
+  const size_t esize = out_dt == FP8_DT_F32 ? 4 : 2;
+  if (K == 0) return hip_status(launch_fill_zero(out, M * N * (int64_t)esize, stream));
+  if (!a || !b || !a_scales || !b_scales) return FP8_ERR_NULL;
+  if (kind == FP4_SCALE_NV && (!a_tensor_scale || !b_tensor_scale)) return FP8_ERR_NULL;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4)) return FP8_ERR_ALIGN;
+  if (kind == FP4_SCALE_NV && (!aligned(a_tensor_scale, 4) || !aligned(b_tensor_scale, 4))) return FP8_ERR_ALIGN;
+  GemmArgs p = GemmArgs{};
+  p.a = a;
+  p.b = b;
+  p.sa = a_scales;
+  p.sb = b_scales;
+  p.ta = a_tensor_scale;
+  p.tb = b_tensor_scale;
+  p.out = out;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.ldo = N;
+  return hip_status(launch_gemm_fp4(p, kind == FP4_SCALE_MX ? MODE_MX4 : MODE_NV4, (int)out_dt, stream));
+}
+
 }  // extern "C"

@@ -39,6 +39,8 @@
 //   MODE_MX        32-element UE8M0 blocks: 2^(eA+eB) applied per 32-K block,
 //                  folded into the bf16 operands (exact path) or given to the
 //                  scaled MFMA (fast path)
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace fp8blk {
@@ -89,7 +91,14 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   constexpr int NW = WMW * WNW;                        // waves
   constexpr int LPW = (TBM + TBN) / 8 / NW;            // 1-KiB loads per wave per K step
   static_assert((TBM + TBN) % (8 * NW) == 0, "rows must split evenly over the waves");
-  constexpr int SCALE_CHUNKS = MODE == MODE_PROMOTE ? TBM / 64 + 1 : (MODE == MODE_MX ? (TBM + TBN) / 64 : 0);
+  // FP4 operands: two codes per byte, so a K step of 128 bytes per row holds 256 K.
+  constexpr bool FP4 = MODE == MODE_MX4 || MODE == MODE_NV4;
+  static_assert(!FP4 || PATH == PATH_EXACT, "FP4 operands take the exact path");
+  // Scale words staged per row and step: FP8 MX 4 bytes (128 K / 32), MXFP4 8
+  // bytes (256 K / 32), NVFP4 16 bytes (256 K / 16).
+  constexpr int SW = MODE == MODE_MX4 ? 2 : (MODE == MODE_NV4 ? 4 : 1);
+  constexpr int SCALE_CHUNKS = MODE == MODE_PROMOTE ? TBM / 64 + 1
+                               : (MODE == MODE_MX || FP4 ? SW * (TBM + TBN) / 64 : 0);
   constexpr int SC = (SCALE_CHUNKS + NW - 1) / NW;     // scale loads per wave per step
   constexpr int LOADS = LPW + SC;                      // loads per wave per step
   static_assert((NS - 1) * LOADS <= 63, "loads in flight must fit the vmcnt counter");
@@ -97,7 +106,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // NS LDS stages; the loads of the next NS-1 K steps are in flight while one is computed.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS][(TBM + TBN) * TBK];
   __shared__ __attribute__((aligned(16))) float s_x[NS][TBM];                    // MODE_PROMOTE: sA[m, kb]
-  __shared__ __attribute__((aligned(16))) uint32_t s_e[NS][TBM + TBN];           // MODE_MX: 4 scale bytes per row
+  __shared__ __attribute__((aligned(16))) uint32_t s_e[NS][SW][TBM + TBN];       // MX / FP4: scale words per row
   __shared__ __attribute__((aligned(16))) float s_w[NS][64];                     // MODE_PROMOTE: sB[n/128, kb]
   __shared__ __attribute__((aligned(16))) uint32_t s_spare[64];                  // target of filler loads
 
@@ -108,7 +117,8 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   const int64_t m0 = tm * TBM, n0 = tn * TBN;
   const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w / WNW, wn = w % WNW;  // wave tile: rows wm*WR.., cols wn*WC..
-  const int nkb = (int)(K / 128);
+  const int64_t KB = FP4 ? K / 2 : K;                  // bytes per operand row
+  const int nkb = (int)(KB / 128);
   const int64_t rows_a = (M - m0) < TBM ? (M - m0) : TBM;
   const int64_t rows_b = (N - n0) < TBN ? (N - n0) : TBN;
 
@@ -121,20 +131,20 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // by a descriptor that starts at its first row and ends after the tile's
   // last valid row (scalar arithmetic, no per-block vector registers).
   const int q8 = lane >> 3;
-  const int goff_even = q8 * (int)K + (((lane & 7) ^ q8) << 4);
-  const int goff_odd = q8 * (int)K + (((lane & 7) ^ q8 ^ 1) << 4);
+  const int goff_even = q8 * (int)KB + (((lane & 7) ^ q8) << 4);
+  const int goff_odd = q8 * (int)KB + (((lane & 7) ^ q8 ^ 1) << 4);
   auto block_rsrc = [&](const uint8_t* base, int64_t rows, int x) {  // x: 8-row block inside its tile
-    return uniform_rsrc(base + 8 * x * K, (rows - 8 * x) * K);
+    return uniform_rsrc(base + 8 * x * KB, (rows - 8 * x) * KB);
   };
-  const uint8_t* a_base = p.a + m0 * K;
-  const uint8_t* b_base = p.b + n0 * K;
+  const uint8_t* a_base = p.a + m0 * KB;
+  const uint8_t* b_base = p.b + n0 * KB;
 
   // Scale descriptors (same row ranges) and per-lane offsets of the staged scales.
-  const int64_t kq = K / 32;
+  const int64_t kq = MODE == MODE_NV4 ? K / 16 : K / 32;   // scale bytes per row
   __amdgpu_buffer_rsrc_t rssa = block_rsrc(a_base, rows_a, 0), rssb = block_rsrc(b_base, rows_b, 0);
   if constexpr (MODE == MODE_PROMOTE)
     rssa = uniform_rsrc(reinterpret_cast<const float*>(p.sa) + m0 * nkb, rows_a * nkb * 4);
-  if constexpr (MODE == MODE_MX) {
+  if constexpr (MODE == MODE_MX || FP4) {
     rssa = uniform_rsrc(reinterpret_cast<const uint8_t*>(p.sa) + m0 * kq, rows_a * kq);
     rssb = uniform_rsrc(reinterpret_cast<const uint8_t*>(p.sb) + n0 * kq, rows_b * kq);
   }
@@ -170,16 +180,20 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
           dma_to_lds<4>(rssw, lds_addr(&s_spare[0]), kOutOfRange);
       }
     }
-    if constexpr (MODE == MODE_MX) {
+    if constexpr (MODE == MODE_MX || FP4) {
+      constexpr int RC = (TBM + TBN) / 64;   // row chunks; word wd of every row chunk is a chunk of its own
 #pragma unroll
       for (int t2 = 0; t2 < SC; ++t2) {
-        const int c = w + NW * t2;   // chunks of 64 rows: A rows first, then B rows
-        if (c < TBM / 64)
-          dma_to_lds<4>(rssa, lds_addr(&s_e[buf][64 * c]), (int)((64 * c + lane) * kq + kb * 4));
-        else if (c < (TBM + TBN) / 64)
-          dma_to_lds<4>(rssb, lds_addr(&s_e[buf][64 * c]), (int)((64 * c - TBM + lane) * kq + kb * 4));
-        else
+        const int c = w + NW * t2;   // chunks of 64 rows: A rows first, then B rows, word by word
+        const int wd = c / RC, rc = c - wd * RC;
+        if (c >= SW * RC)
           dma_to_lds<4>(rssb, lds_addr(&s_spare[0]), kOutOfRange);
+        else if (rc < TBM / 64)
+          dma_to_lds<4>(rssa, lds_addr(&s_e[buf][wd][64 * rc]),
+                        (int)((64 * rc + lane) * kq + kb * 4 * SW + 4 * wd));
+        else
+          dma_to_lds<4>(rssb, lds_addr(&s_e[buf][wd][64 * rc]),
+                        (int)((64 * rc - TBM + lane) * kq + kb * 4 * SW + 4 * wd));
       }
     }
   };
@@ -251,7 +265,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       for (int j = 0; j < NJ; ++j) {
         const int r = b_row0 + 16 * j;
         fb[j] = join(lds16(sb_, r * 128 + c0), lds16(sb_, r * 128 + c1));
-        if constexpr (MODE == MODE_MX) eb[j] = (int)((s_e[buf][TBM + r] >> (8 * g)) & 0xffu);
+        if constexpr (MODE == MODE_MX) eb[j] = (int)((s_e[buf][0][TBM + r] >> (8 * g)) & 0xffu);
       }
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
@@ -267,7 +281,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
             for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(pr[q], kWaveWScale ? sc[q] : sc[q] * swj[j], acc[i][j][q]);
           }
         } else if constexpr (MODE == MODE_MX) {
-          const int ea = (int)((s_e[buf][r] >> (8 * g)) & 0xffu);
+          const int ea = (int)((s_e[buf][0][r] >> (8 * g)) & 0xffu);
 #pragma unroll
           for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_fp8<AF, BF>(fa, fb[j], acc[i][j], ea, eb[j]);
         } else {
@@ -276,13 +290,62 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
             acc[i][j] = mfma_fp8<AF, BF>(fa, fb[j], acc[i][j], (int)kUnitScale, (int)kUnitScale);
         }
       }
+    } else if constexpr (FP4) {
+      // FP4 exact path: the lane's two 16-byte chunks (2g, 2g+1) hold K
+      // 64g..64g+63 of this 256-K step; each chunk is 32 codes, four matrix
+      // operands of 8 (byte i of a word holds codes 2i, 2i+1 in its low and
+      // high nibble).  Every code times its block scale is exact:
+      //   MX: bf16 operands, 2^e applied by the convert (block 2g+h of the
+      //       step, one per chunk);
+      //   NV: fp16 operands, the E4M3 microscale applied by a packed fp16
+      //       multiply (the scaled converts keep only a scale's exponent);
+      //       words 0-1 and 2-3 of a chunk are blocks 4g+2h and 4g+2h+1,
+      //       bytes 2h and 2h+1 of staged word g.
+      using Op = typename std::conditional<MODE == MODE_NV4, v8h, v8bf>::type;
+      auto frag = [&](const uint8_t* base, int row, int R, int h, Op* x) {
+        const u32x4 d = lds16(base, row * 128 + (h ? c1 : c0));
+        if constexpr (MODE == MODE_MX4) {
+          const int bi = 2 * g + h;
+          const float sc = e8m0_to_f32((s_e[buf][bi >> 2][R] >> (8 * (bi & 3))) & 0xffu);
+          x[0] = cvt8_fp4(d.x, sc);
+          x[1] = cvt8_fp4(d.y, sc);
+          x[2] = cvt8_fp4(d.z, sc);
+          x[3] = cvt8_fp4(d.w, sc);
+        } else {
+          const v2f m = h ? decode2<FMT_E4M3>(s_e[buf][g][R], true) : decode2<FMT_E4M3>(s_e[buf][g][R], false);
+          const v2h m0 = {(_Float16)m.x, (_Float16)m.x}, m1 = {(_Float16)m.y, (_Float16)m.y};
+          x[0] = cvt8_fp4_f16(d.x, m0);
+          x[1] = cvt8_fp4_f16(d.y, m0);
+          x[2] = cvt8_fp4_f16(d.z, m1);
+          x[3] = cvt8_fp4_f16(d.w, m1);
+        }
+      };
+      auto mma = [](const Op& a, const Op& b, const v4f& c) {
+        if constexpr (MODE == MODE_NV4) return mfma_f16(a, b, c);
+        else return mfma_bf16(a, b, c);
+      };
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        Op xb[NJ][4];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) frag(sb_, b_row0 + 16 * j, TBM + b_row0 + 16 * j, h, xb[j]);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          Op xa[4];
+          frag(sa_, a_row0 + 16 * i, a_row0 + 16 * i, h, xa);
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[i][j] = mma(xa[s], xb[j][s], acc[i][j]);
+        }
+      }
     } else {
       // Exact path: four K=32 sub-steps on bf16 operands (MX scales folded in).
       v8bf xb[NJ][4];
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int r = b_row0 + 16 * j;
-        const float fsb = (MODE == MODE_MX) ? e8m0_to_f32((s_e[buf][TBM + r] >> (8 * g)) & 0xffu) : 1.0f;
+        const float fsb = (MODE == MODE_MX) ? e8m0_to_f32((s_e[buf][0][TBM + r] >> (8 * g)) & 0xffu) : 1.0f;
         const u32x4 d0 = lds16(sb_, r * 128 + c0), d1 = lds16(sb_, r * 128 + c1);
         xb[j][0] = cvt8<BF>(d0.x, d0.y, fsb);
         xb[j][1] = cvt8<BF>(d0.z, d0.w, fsb);
@@ -346,7 +409,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           const int r = a_row0 + 16 * i;
-          const float fsa = (MODE == MODE_MX) ? e8m0_to_f32((s_e[buf][r] >> (8 * g)) & 0xffu) : 1.0f;
+          const float fsa = (MODE == MODE_MX) ? e8m0_to_f32((s_e[buf][0][r] >> (8 * g)) & 0xffu) : 1.0f;
           const u32x4 d0 = lds16(sa_, r * 128 + c0), d1 = lds16(sa_, r * 128 + c1);
           v8bf xa[4];
           xa[0] = cvt8<AF>(d0.x, d0.y, fsa);
@@ -434,11 +497,13 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         const int64_t col = cbase + (lane & 15);
         float sbv = 1.0f;
         if constexpr (MODE == MODE_EPILOGUE) sbv = swb[p.b_per_row ? col : 0];
+        if constexpr (MODE == MODE_NV4) sbv = p.ta[0] * p.tb[0];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t row = rbase + 4 * g + q;
           float v = acc[i][j][q];
           if constexpr (MODE == MODE_EPILOGUE) v = v * (sxa[p.a_per_row ? row : 0] * sbv);
+          if constexpr (MODE == MODE_NV4) v = v * sbv;
           store_out<ODT>(p.out, row * p.ldo + col, v);
         }
       }
@@ -459,9 +524,11 @@ template <int AF, int BF, int MODE, int ODT, int PATH>
 __global__ __launch_bounds__(512, 1) void k_gemm_tiled_256x192(GemmArgs p) {
   gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 8, 3, 2>(p);
 }
+// (NVFP4 stages 16 scale bytes per row and step: three stages would exceed
+// the 160 KiB of LDS, so it runs two.)
 template <int AF, int BF, int MODE, int ODT, int PATH>
 __global__ __launch_bounds__(512, 1) void k_gemm_tiled_128x256(GemmArgs p) {
-  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 4, 4, 3>(p);
+  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 4, 4, MODE == MODE_NV4 ? 2 : 3>(p);
 }
 
 
@@ -493,11 +560,13 @@ hipError_t launch_fill_f32(float* out, int64_t n, float v, hipStream_t st) {
 // multiple of 128, so every scale layout splits at a block boundary).
 static GemmArgs column_range(const GemmArgs& p, int64_t c0, int64_t n, int mode, int odt) {
   GemmArgs q = p;
-  q.b = p.b + c0 * p.K;
+  const bool fp4 = mode == MODE_MX4 || mode == MODE_NV4;
+  q.b = p.b + c0 * (fp4 ? p.K / 2 : p.K);
   q.N = n;
   q.out = static_cast<uint8_t*>(p.out) + c0 * (odt == DT_F32 ? 4 : 2);
   if (mode == MODE_PROMOTE) q.sb = static_cast<const float*>(p.sb) + (c0 / 128) * (p.K / 128);
-  else if (mode == MODE_MX) q.sb = static_cast<const uint8_t*>(p.sb) + c0 * (p.K / 32);
+  else if (mode == MODE_MX || mode == MODE_MX4) q.sb = static_cast<const uint8_t*>(p.sb) + c0 * (p.K / 32);
+  else if (mode == MODE_NV4) q.sb = static_cast<const uint8_t*>(p.sb) + c0 * (p.K / 16);
   else if (p.b_per_row) q.sb = static_cast<const float*>(p.sb) + c0;
   return q;
 }
@@ -554,6 +623,18 @@ static void tiled_mode(const GemmArgs& p, int mode, int odt, int path, hipStream
   if (mode == MODE_EPILOGUE) tiled_odt<AF, BF, MODE_EPILOGUE>(p, odt, path, st);
   else if (mode == MODE_PROMOTE) tiled_odt<AF, BF, MODE_PROMOTE>(p, odt, path, st);
   else tiled_odt<AF, BF, MODE_MX>(p, odt, path, st);
+}
+
+hipError_t launch_gemm_fp4(const GemmArgs& p, int mode, int odt, hipStream_t st) {
+  // the format template arguments are unused by the FP4 modes
+  if (mode == MODE_MX4) {
+    if (odt == DT_F32) tiled_shape<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_F32, PATH_EXACT>(p, st);
+    else tiled_shape<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_BF16, PATH_EXACT>(p, st);
+  } else {
+    if (odt == DT_F32) tiled_shape<FMT_E4M3, FMT_E4M3, MODE_NV4, DT_F32, PATH_EXACT>(p, st);
+    else tiled_shape<FMT_E4M3, FMT_E4M3, MODE_NV4, DT_BF16, PATH_EXACT>(p, st);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_tiled(const GemmArgs& p, int afmt, int bfmt, int mode, int odt, int path, hipStream_t st) {

@@ -11,6 +11,8 @@ namespace fp8blk {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t kUnitScale = 0x7f7f7f7fu;  // E8M0 127 = 2^0 in every byte
 // Word 3 of a gfx9 buffer descriptor for raw byte-addressed access.
@@ -78,6 +80,9 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c
 __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ v4f mfma_f16(const v8h& a, const v8h& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ v8i join(const u32x4& lo, const u32x4& hi) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -96,6 +101,29 @@ __device__ __forceinline__ v2bf cvt2(uint32_t w, float scale, bool hi) {
 }
 
 // The 8 codes of dwords (d0, d1) -> one K=32 bf16 operand.
+// Eight E2M1 codes (one word, code 2i in the low nibble of byte i) to bf16,
+// times `scale`, a power of two: the scaled converts apply the exponent of
+// their scale operand only (measured), which is exact for 2^e in bf16's range.
+__device__ __forceinline__ v8bf cvt8_fp4(uint32_t w, float scale) {
+  const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Eight E2M1 codes to fp16, times an E4M3 microscale m (given as the fp16
+// pair {m, m}): exact converts (scale 1) and a packed fp16 multiply, exact too
+// since a code times an E4M3 value has at most 6 significant bits and lies in
+// [2^-10, 2688].
+__device__ __forceinline__ v8h cvt8_fp4_f16(uint32_t w, v2h m) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * m;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * m;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * m;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * m;
+  return v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 template <int FMT>
 __device__ __forceinline__ v8bf cvt8(uint32_t d0, uint32_t d1, float scale) {
   const v2bf p0 = cvt2<FMT>(d0, scale, false), p1 = cvt2<FMT>(d0, scale, true);

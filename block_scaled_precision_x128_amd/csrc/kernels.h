@@ -12,6 +12,9 @@ namespace fp8blk {
 constexpr int kTensorPartials = 8192;
 
 enum { MODE_EPILOGUE = 0, MODE_PROMOTE = 1, MODE_MX = 2 };
+// FP4 (E2M1, two codes per byte) operands: MXFP4 (UE8M0 per 32 K) and NVFP4
+// (E4M3 microscale per 16 K, fp32 tensor scales ta, tb).
+enum { MODE_MX4 = 3, MODE_NV4 = 4 };
 // Matrix-core path: exact products with fp32 sums (bf16 instructions on the
 // expanded codes), or the FP8 instructions' own accumulation.
 enum { PATH_EXACT = 0, PATH_FAST = 1 };
@@ -26,6 +29,8 @@ struct GemmArgs {
   const void* sb;     // scales of b
   void* out;          // [M, N] values, or codes for the quantized outputs
   float* out_scales;  // quantized outputs: [M, N/128] fp32 tile scales
+  const float* ta;    // MODE_NV4: tensor scale of a (1 float)
+  const float* tb;    // MODE_NV4: tensor scale of b
   int64_t M, N, K;
   int64_t ldo;        // elements between consecutive rows of out (>= N)
   int a_per_row;      // epilogue mode: 1 = one scale per row of a, 0 = one per tensor
@@ -43,6 +48,8 @@ hipError_t launch_dequantize(const uint8_t* q, const void* scales, int64_t rows,
                              void* y, int odt, hipStream_t st);
 hipError_t launch_gemm_tiled(const GemmArgs& p, int afmt, int bfmt, int mode, int odt, int path, hipStream_t st);
 hipError_t launch_gemm_skinny(const GemmArgs& p, int afmt, int bfmt, int mode, int odt, int path, hipStream_t st);
+// FP4 operands (mode MODE_MX4 or MODE_NV4, odt DT_F32 / DT_BF16, K % 256 == 0).
+hipError_t launch_gemm_fp4(const GemmArgs& p, int mode, int odt, hipStream_t st);
 hipError_t launch_fill_zero(void* out, int64_t bytes, hipStream_t st);     // bytes % 4 == 0, 4-byte aligned
 hipError_t launch_fill_f32(float* out, int64_t n, float v, hipStream_t st);
 

@@ -330,6 +330,27 @@ fp8_status_t fp4_dequantize(const uint8_t* q, const uint8_t* block_scales, const
                             int64_t rows, int64_t cols, fp4_scaling_t kind, void* y, fp8_dtype_t y_dt,
                             hipStream_t stream);
 
+/* FP4 block-scaled GEMM: out[m, n] = sum_k deq(a[m, k]) deq(b[n, k]) for
+ * packed E2M1 operands a [M, K/2] and b [N, K/2] (both K-contiguous) of the
+ * same kind:
+ *   FP4_SCALE_MX  sum_k qa 2^ea qb 2^eb      (a_scales [M, K/32], b_scales [N, K/32])
+ *   FP4_SCALE_NV  s_ta s_tb sum_k (qa ma)(qb mb)   (E4M3 microscales [M, K/16],
+ *                 [N, K/16]; tensor scales a_tensor_scale, b_tensor_scale)
+ * ("Illustrated GPU kernels, Part 8", "Low precision: FP8, FP4, and
+ * microscaling": the scale factors travel with the data into the matrix
+ * multiply.)  Products are formed exactly (each code times its block scale is
+ * exact in bf16) and summed in fp32 on the bf16 matrix cores; the NV tensor
+ * scales multiply the fp32 result.  Meets |out - exact| <= 1e-4 sum_k |deq
+ * products| (plus half a bf16 ulp for bf16 output) while every code times its
+ * scale stays inside bf16's range (MX exponents below 127).
+ * Shapes: M % 16 == 0, N % 16 == 0, K % 256 == 0, K <= 2^22.  a, b, out
+ * 16-byte aligned; scale arrays 4-byte aligned.  out_dt FP8_DT_F32 or
+ * FP8_DT_BF16.  K == 0 writes zeros. */
+fp8_status_t fp4_gemm_blockscaled(const uint8_t* a, const uint8_t* a_scales, const float* a_tensor_scale,
+                                  const uint8_t* b, const uint8_t* b_scales, const float* b_tensor_scale,
+                                  int64_t M, int64_t N, int64_t K, fp4_scaling_t kind, void* out,
+                                  fp8_dtype_t out_dt, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -223,6 +223,10 @@ def dequant_exact(kind: int, packed, scales, s_t=None) -> np.ndarray:
     return (q.reshape(rows, K // NV_BLOCK, NV_BLOCK) * m[..., None]).reshape(rows, K)
 
 
+def _scalar32(v) -> np.float32:
+    return np.float32(np.asarray(v, dtype=np.float32).reshape(-1)[0])
+
+
 def gemm_ref(kind: int, a, sa, b, sb, ta=None, tb=None):
     """(Ref, Abs) in fp64: Ref = sum_k deq(a) deq(b) (NV: times s_ta s_tb),
     Abs = the same sum of absolute values (the tolerance's scale)."""
@@ -231,7 +235,7 @@ def gemm_ref(kind: int, a, sa, b, sb, ta=None, tb=None):
     ref = xa @ xb.T
     absb = np.abs(xa) @ np.abs(xb).T
     if kind == NV:
-        t = float(np.float32(ta)) * float(np.float32(tb))
+        t = float(_scalar32(ta)) * float(_scalar32(tb))
         ref, absb = ref * t, absb * t
     return ref, absb
 
@@ -256,6 +260,6 @@ def gemm_exact_fraction(kind: int, a, sa, b, sb, ta=None, tb=None):
             for k in range(K):
                 acc += val(qa, sa, i, k) * val(qb, sb, j, k)
             if kind == NV:
-                acc *= Fraction(float(np.float32(ta))) * Fraction(float(np.float32(tb)))
+                acc *= Fraction(float(_scalar32(ta))) * Fraction(float(_scalar32(tb)))
             out[i][j] = acc
     return out

@@ -226,3 +226,21 @@ def test_library_exports_nothing_else(lib):
     out = subprocess.run([nm, "-D", "--defined-only", fb.LIB_PATH], capture_output=True, text=True, check=True).stdout
     c_syms = sorted(l.split()[-1] for l in out.splitlines() if " T " in l and not l.split()[-1].startswith("_Z"))
     assert c_syms == header_functions()
+
+
+def test_fp4_gemm_validation(lib):
+    f = lib.fp4_gemm_blockscaled
+    args = lambda a=FAKE, sa=FAKE, ta=FAKE, b=FAKE, sb=FAKE, tb=FAKE, M=32, N=32, K=512, kind=1, out=FAKE, odt=0: (
+        a, sa, ta, b, sb, tb, M, N, K, kind, out, odt, None)
+    assert f(*args(kind=2)) == 2
+    assert f(*args(odt=2)) == 2
+    assert f(*args(K=384)) == 3               # K % 256
+    assert f(*args(M=24)) == 3
+    assert f(*args(K=1 << 23)) == 3
+    assert f(*args(ta=None)) == 1             # NV needs the tensor scales
+    assert f(*args(sb=None)) == 1
+    assert f(*args(out=None)) == 1
+    assert f(*args(a=FAKE + 8)) == 7
+    assert f(*args(sa=FAKE + 2)) == 7
+    assert f(*args(kind=0, ta=None, tb=None, a=FAKE + 8)) == 7   # MX ignores the tensor scales
+    assert f(*args(M=0, a=None, out=None)) == 0

@@ -1,0 +1,93 @@
+"""GPU parity: FP4 (E2M1) block-scaled GEMM, MXFP4 and NVFP4, against the
+oracle's fp64 reference.  Operands are quantized by the oracle on the CPU and
+the same codes and scales go to both sides.  Bound: |out - Ref| <= 1e-4 *
+sum_k |deq(a) deq(b)| per element, plus half a bf16 ulp for bf16 outputs.
+
+Shapes cover the three tile configurations: small problems (128x256 tiles),
+4096x4096 (256x256) and 4096x4480 (256x256 plus a 256x192 column remainder),
+with ragged M and N."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_precision_x128_amd as fb
+import workloads
+from oracle import fp4
+from gpu_helpers import dev, gemm_check, host, say
+
+pytestmark = pytest.mark.gpu
+
+KINDS = [fb.FP4_MX, fb.FP4_NV]
+
+
+def _operands(kind, M, N, K, seed, wide=False):
+    rng = np.random.default_rng(seed)
+    wl = workloads.CONFIGS["c3_deepseek_block"]
+    x = workloads.draw_x(wl, M, K, rng)
+    w = workloads.draw_w(wl, N, K, rng)
+    if wide:   # rows spanning many binades: the block scales differ widely along K
+        x = (x * np.exp(rng.uniform(-8, 8, (1, K))).astype(np.float32)).astype(np.float32)
+    if kind == fb.FP4_MX:
+        a, sa = fp4.quantize_mx(x)
+        b, sb = fp4.quantize_mx(w)
+        return a, sa, None, b, sb, None
+    a, sa, ta = fp4.quantize_nv(x)
+    b, sb, tb = fp4.quantize_nv(w)
+    return a, sa, np.array([ta], np.float32), b, sb, np.array([tb], np.float32)
+
+
+def _run(kind, ops, out_dt):
+    a, sa, ta, b, sb, tb = ops
+    out = fb.fp4_gemm_blockscaled(dev(a), dev(sa), None if ta is None else dev(ta), dev(b), dev(sb),
+                                  None if tb is None else dev(tb), kind, out_dt)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("out_dt", [fb.DT_F32, fb.DT_BF16])
+@pytest.mark.parametrize("shape", [(16, 16, 256), (48, 80, 512), (272, 528, 768), (512, 1024, 2048)])
+def test_fp4_gemm_small(kind, out_dt, shape):
+    M, N, K = shape
+    label = f"fp4 gemm kind={kind} out={out_dt} shape={shape}"
+    say(label)
+    ops = _operands(kind, M, N, K, 900 + kind + M + N)
+    out = _run(kind, ops, out_dt)
+    ref, absb = fp4.gemm_ref(kind, ops[0], ops[1], ops[3], ops[4], ops[2], ops[5])
+    gemm_check(out, out_dt, ref, absb, label)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_fp4_gemm_wide_scales(kind):
+    label = f"fp4 gemm wide scales kind={kind}"
+    say(label)
+    ops = _operands(kind, 64, 128, 1024, 950 + kind, wide=True)
+    out = _run(kind, ops, fb.DT_F32)
+    ref, absb = fp4.gemm_ref(kind, ops[0], ops[1], ops[3], ops[4], ops[2], ops[5])
+    gemm_check(out, fb.DT_F32, ref, absb, label)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("N", [4096, 4480])
+def test_fp4_gemm_large_tiles(kind, N):
+    """4096 x N x 256: 256x256 tiles (N = 4096) and the column split (N = 4480);
+    every output is checked."""
+    M, K = 4096, 256
+    label = f"fp4 gemm large kind={kind} shape={(M, N, K)}"
+    say(label)
+    ops = _operands(kind, M, N, K, 970 + kind + N)
+    out = _run(kind, ops, fb.DT_BF16)
+    ref, absb = fp4.gemm_ref(kind, ops[0], ops[1], ops[3], ops[4], ops[2], ops[5])
+    gemm_check(out, fb.DT_BF16, ref, absb, label)
+
+
+def test_fp4_gemm_k_zero():
+    say("fp4 gemm K=0")
+    a = torch.zeros((32, 0), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((32, 0), dtype=torch.uint8, device="cuda")
+    out = torch.full((32, 48), 7.0, device="cuda")
+    b = torch.zeros((48, 0), dtype=torch.uint8, device="cuda")
+    fb.fp4_gemm_blockscaled(a, s, None, b, s[:0], None, fb.FP4_MX, fb.DT_F32, out=out)
+    torch.cuda.synchronize()
+    assert not host(out).any()
