@@ -24,6 +24,10 @@ reads data another launch left in the 256 MB last-level cache.
 For the decode workload (c4_decode_skinny) W is quantized once per input set
 in setup, as a model's weights are, and a step is quantize X + GEMM.
 
+The FP4 workloads (--workload fp4_mx_4096x7168x7168 / fp4_nv_4096x7168x7168:
+the DeepSeek shape and inputs with E2M1 operands, MXFP4 or NVFP4 scales) run
+quantize X + quantize W + GEMM + dequantize X the same way.
+
 The FP8 KV-cache workload (--workload kv_llama8b_b32_ctx8k: 32 sequences of
 8192 tokens, 8 KV heads of 128, bf16 states, E4M3 codes with per-channel
 scales, a paged pool in random block order) has a step of its own: append
@@ -381,13 +385,153 @@ def bench_kv(args, wl) -> int:
     return 0
 
 
+# ---- FP4 (E2M1) microscaling --------------------------------------------------
+
+def fp4_cpu_baseline(wl, x_rows: int, w_rows: int):
+    """The oracle on the host: FP4 quantize of a sample of X and W rows, the
+    fp64 GEMM of the sample, dequantize of the X sample; TFLOP/s of 2 m n K."""
+    from oracle import fp4 as ofp4
+    xs, ws = workloads.make_inputs(wl, M=x_rows, N=w_rows)
+    x = workloads.storage_to_f32(xs, wl.in_dtype)
+    w = workloads.storage_to_f32(ws, wl.in_dtype)
+    t0 = time.perf_counter()
+    if wl.fp4_kind == workloads.FP4_MX:
+        a, sa = ofp4.quantize_mx(x)
+        b, sb = ofp4.quantize_mx(w)
+        ta = tb = None
+        ofp4.gemm_ref(ofp4.MX, a, sa, b, sb)
+        ofp4.dequantize_mx(a, sa)
+    else:
+        a, sa, ta = ofp4.quantize_nv(x)
+        b, sb, tb = ofp4.quantize_nv(w)
+        ofp4.gemm_ref(ofp4.NV, a, sa, b, sb, ta, tb)
+        ofp4.dequantize_nv(a, sa, ta)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    flops = 2.0 * x_rows * w_rows * wl.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{x_rows} of {wl.M} rows of X and {w_rows} of {wl.N} rows of W: oracle FP4 quantize of "
+                      f"both, fp64 GEMM of the sample (numpy BLAS threads={threads}), dequantize of X; "
+                      f"{dt:.2f} s"}
+
+
+def bench_fp4(args, wl) -> int:
+    import torch
+    import block_scaled_precision_x128_amd as fb
+
+    fb.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    M, N, K, kind = wl.M, wl.N, wl.K, wl.fp4_kind
+    xs_np, ws_np = workloads.make_inputs(wl)
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    x0, w0 = to_dev(xs_np), to_dev(ws_np)
+    del xs_np, ws_np
+    blk = fb.fp4_block(kind)
+    set_bytes = (M + N) * K * 2.5 + M * N * 2 + M * K * 2
+    R = args.sets or max(2, int(np.ceil(1.2e9 / set_bytes)))
+    sets = []
+    for r in range(R):
+        x = x0 if r == 0 else x0.clone()
+        w = w0 if r == 0 else w0.clone()
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+        xs = torch.empty((M, K // blk), dtype=torch.uint8, device=dev)
+        wsc = torch.empty((N, K // blk), dtype=torch.uint8, device=dev)
+        xt = torch.empty(1, dtype=torch.float32, device=dev) if kind == fb.FP4_NV else None
+        wt = torch.empty(1, dtype=torch.float32, device=dev) if kind == fb.FP4_NV else None
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        xr = torch.empty_like(x)
+        sets.append((x, w, xq, wq, xs, wsc, xt, wt, out, xr))
+    wsx = torch.empty(max(1, fb.fp4_quantize_workspace_bytes(M, K, kind)), dtype=torch.uint8, device=dev)
+    wsw = torch.empty(max(1, fb.fp4_quantize_workspace_bytes(N, K, kind)), dtype=torch.uint8, device=dev)
+
+    qx = lambda st: fb.fp4_quantize(st[0], kind, q=st[2], block_scales=st[4], tensor_scale=st[6], workspace=wsx,
+                                    stream=stream)
+    qw = lambda st: fb.fp4_quantize(st[1], kind, q=st[3], block_scales=st[5], tensor_scale=st[7], workspace=wsw,
+                                    stream=stream)
+    gm = lambda st: fb.fp4_gemm_blockscaled(st[2], st[4], st[6], st[3], st[5], st[7], kind, fb.DT_BF16, out=st[8],
+                                            stream=stream)
+    dq = lambda st: fb.fp4_dequantize(st[2], st[4], st[6], kind, fb.DT_BF16, y=st[9], stream=stream)
+
+    def step(i):
+        st = sets[i % R]
+        qx(st)
+        qw(st)
+        gm(st)
+        dq(st)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    def events_ms(fn, reps):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(20_000_000)       # keep the GPU busy while the launches are queued
+        t0.record(stream)
+        for i in range(reps):
+            fn(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    wall0 = time.perf_counter()
+    ms_step = events_ms(step, args.steps)
+    wall = time.perf_counter() - wall0
+    at = lambda f: (lambda i: f(sets[(args.warmup + i) % R]))
+    qx_ms, qw_ms, gm_ms, dq_ms = (events_ms(at(f), args.steps) for f in (qx, qw, gm, dq))
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops / (gm_ms * 1e-3) / 1e12
+    qbytes = lambda rows: rows * K * 2 + rows * K // 2 + rows * (K // blk)
+    traffic = read_traffic(wl.name, "fp32")
+    result = {
+        "metric": "block-scaled FP4 GEMM TFLOP/s (exact products, fp32 sums); quantize GB/s",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4",
+        "data": "synthetic (seeded; bf16 activations ~N(0,1) with outlier channels, weights ~N(0,0.02))",
+        "config": {"workload": f"{wl.name}: M={M} N={N} K={K}, E2M1 operands, "
+                               + ("MXFP4 (UE8M0 per 32)" if kind == fb.FP4_MX else
+                                  "NVFP4 (E4M3 per 16 + fp32 tensor scale)") + ", bf16 out",
+                   "step": "quantize X + quantize W + GEMM + dequantize X",
+                   "rotated_input_sets": R,
+                   "accumulation": "codes times block scales expanded exactly to "
+                                   + ("bf16" if kind == fb.FP4_MX else "fp16") + ", matrix cores, fp32 sums"},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "kernels": {"gemm_ms": round(gm_ms, 4), "gemm_tflops": round(gemm_tflops, 1),
+                    "quantize_x_ms": round(qx_ms, 4), "quantize_x_gbs": round(qbytes(M) / (qx_ms * 1e-3) / 1e9, 1),
+                    "quantize_w_ms": round(qw_ms, 4), "quantize_w_gbs": round(qbytes(N) / (qw_ms * 1e-3) / 1e9, 1),
+                    "dequantize_x_ms": round(dq_ms, 4),
+                    "dequantize_x_gbs": round((M * K // 2 + M * (K // blk) + M * K * 2) / (dq_ms * 1e-3) / 1e9, 1)},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = fp4_cpu_baseline(wl, 1024, 4096)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3_deepseek_block",
-                    choices=workloads.CONFIG_ORDER + list(workloads.KV_CONFIGS))
+                    choices=workloads.CONFIG_ORDER + list(workloads.KV_CONFIGS) + list(workloads.FP4_CONFIGS))
     ap.add_argument("--sets", type=int, default=0, help="rotated input sets (0 = enough for 1 GB)")
     ap.add_argument("--accum", choices=["fp32", "native"], default="fp32",
                     help="GEMM accumulation: exact products with fp32 sums (default) or the FP8 "
@@ -444,6 +588,8 @@ def main(argv=None) -> int:
 
     if args.workload in workloads.KV_CONFIGS:
         return bench_kv(args, workloads.KV_CONFIGS[args.workload])
+    if args.workload in workloads.FP4_CONFIGS:
+        return bench_fp4(args, workloads.FP4_CONFIGS[args.workload])
 
     wl = workloads.CONFIGS[args.workload]
     accum = fb.ACCUM_NATIVE if args.accum == "native" else fb.ACCUM_FP32

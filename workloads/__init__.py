@@ -69,6 +69,7 @@ class Workload:
     x_outlier_factor: float
     w_kind: str            # "normal" (sigma 0.02) or "loguniform" (|w| = 10^U(-6,3))
     x_outlier_count: Optional[int] = None  # exact count when the page fixes it
+    fp4_kind: Optional[int] = None         # FP4 workloads: FP4_MX or FP4_NV (formats and granularities unused)
 
     def n_outliers(self, K: Optional[int] = None) -> int:
         K = self.K if K is None else K
@@ -102,6 +103,19 @@ CONFIGS = {
 
 CONFIG_ORDER = ["c1_per_tensor", "c2_per_token_channel", "c3_deepseek_block",
                 "c4_decode_skinny", "c5_mxfp8_mix"]
+
+# FP4 (E2M1) microscaling at the DeepSeek block-scaled shape and inputs
+# ("Illustrated GPU kernels, Part 8": MXFP4 blocks of 32, NVFP4 blocks of 16
+# with an E4M3 microscale and a tensor scale).
+FP4_MX, FP4_NV = 0, 1
+FP4_CONFIGS = {
+    "fp4_mx_4096x7168x7168": Workload(
+        "fp4_mx_4096x7168x7168", 103, 4096, 7168, 7168, DT_BF16, E4M3, E4M3,
+        GRAN_MX32, GRAN_MX32, DT_BF16, 0.005, 100.0, "normal", fp4_kind=FP4_MX),
+    "fp4_nv_4096x7168x7168": Workload(
+        "fp4_nv_4096x7168x7168", 103, 4096, 7168, 7168, DT_BF16, E4M3, E4M3,
+        GRAN_MX32, GRAN_MX32, DT_BF16, 0.005, 100.0, "normal", fp4_kind=FP4_NV),
+}
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
