@@ -175,4 +175,44 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return r;
 }
 
+// Max of p[0..n) over one wave, eight independent loads in flight per lane
+// (values >= 0 or NaN; fmaxf skips NaN, an empty input gives 0); result in
+// every lane.
+__device__ __forceinline__ float wave_max_of(const float* __restrict__ p, int64_t n) {
+  const int lane = threadIdx.x & 63;
+  float m[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) m[u] = 0.0f;
+  int64_t i = lane;
+  for (; i + 7 * 64 < n; i += 8 * 64) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m[u] = fmaxf(m[u], p[i + u * 64]);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (i + u * 64 < n) m[u] = fmaxf(m[u], p[i + u * 64]);
+  return wave_max(fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])), fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7]))));
+}
+
+// Max of p[0..n) over the workgroup (values >= 0 or NaN; fmaxf skips NaN, so
+// an all-NaN or empty input gives 0), result in every thread.  Each thread
+// keeps eight independent loads in flight: a loop with one load per trip
+// waits a memory latency per element it visits.
+__device__ __forceinline__ float block_max_of(const float* __restrict__ p, int64_t n, float* red) {
+  const int64_t T = blockDim.x;
+  float m[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) m[u] = 0.0f;
+  int64_t i = threadIdx.x;
+  for (; i + 7 * T < n; i += 8 * T) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m[u] = fmaxf(m[u], p[i + u * T]);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (i + u * T < n) m[u] = fmaxf(m[u], p[i + u * T]);
+  const float r = fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])), fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7])));
+  return block_max(r, red);
+}
+
 }  // namespace fp8blk

@@ -106,9 +106,7 @@ __global__ __launch_bounds__(256) void k_fp4_quant_nv(const void* __restrict__ x
                                                        int64_t nch, const float* __restrict__ partial,
                                                        int npartial) {
   __shared__ float red[16];
-  float mt = 0.0f;
-  for (int i = threadIdx.x; i < npartial; i += 256) mt = fmaxf(mt, partial[i]);
-  mt = block_max(mt, red);
+  const float mt = block_max_of(partial, npartial, red);
   float st = mt / 2688.0f;   // correctly rounded
   st = st == 0.0f ? 1.0f : st;
   if (blockIdx.x == 0 && threadIdx.x == 0) ts[0] = st;

@@ -192,9 +192,7 @@ __global__ __launch_bounds__(256) void k_quant_tensor(const void* __restrict__ x
                                                        float* __restrict__ scales, int64_t nch,
                                                        const float* __restrict__ partial, int npartial) {
   __shared__ float red[16];
-  float m = 0.0f;
-  for (int i = threadIdx.x; i < npartial; i += 256) m = fmaxf(m, partial[i]);
-  m = block_max(m, red);
+  const float m = block_max_of(partial, npartial, red);
   const float s = group_scale<FMT>(m);
   for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < nch; idx += (int64_t)gridDim.x * 256) {
     float v[8];
@@ -218,31 +216,27 @@ template <int FMT>
 __global__ __launch_bounds__(256) void k_delayed_scale(const float* __restrict__ hist, int64_t len, int margin,
                                                         float* __restrict__ scale) {
   __shared__ float red[16];
-  float m = 0.0f;
-  for (int64_t i = threadIdx.x; i < len; i += 256) m = fmaxf(m, hist[i]);  // fmaxf skips NaN entries
-  m = block_max(m, red);
+  const float m = block_max_of(hist, len, red);  // NaN entries are skipped
   if (threadIdx.x == 0) {
     const float s = m / __builtin_amdgcn_ldexpf(Fp8Limits<FMT>::vmax, -margin);  // correctly rounded
     *scale = s == 0.0f ? 1.0f : s;
   }
 }
 
-// Encodes under the history's scale and reduces the tensor's amax per wave
-// (no LDS, no barrier).  With a short history (FOLD) every wave derives the
-// scale itself from the history, which saves the separate scale kernel's
-// launch; the first wave writes it out.  Each thread keeps 4 chunks of loads
-// in flight.  partial[] holds one maximum per wave.
+// Encodes under the history's scale and reduces the tensor's amax per
+// workgroup.  With a short history (FOLD) every wave derives the scale itself
+// from the history, which saves the separate scale kernel's launch; the first
+// wave writes it out.  Each thread keeps 4 chunks of loads in flight.
+// partial[] holds one maximum per workgroup, so that the one-workgroup
+// reduction after this kernel reads few values.
 template <int FMT, int DT, bool FOLD>
 __global__ __launch_bounds__(256) void k_quant_given_scale(const void* __restrict__ x, uint8_t* __restrict__ q,
                                                             float* __restrict__ scale, const float* __restrict__ hist,
                                                             int64_t len, int margin, int64_t nch,
                                                             float* __restrict__ partial) {
-  const int lane = threadIdx.x & 63;
   float s;
   if constexpr (FOLD) {
-    float hm = 0.0f;
-    for (int64_t i = lane; i < len; i += 64) hm = fmaxf(hm, hist[i]);  // fmaxf skips NaN entries
-    hm = wave_max(hm);
+    const float hm = wave_max_of(hist, len);  // NaN entries are skipped
     const float sv = hm / __builtin_amdgcn_ldexpf(Fp8Limits<FMT>::vmax, -margin);  // correctly rounded
     s = sv == 0.0f ? 1.0f : sv;
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
@@ -267,16 +261,15 @@ __global__ __launch_bounds__(256) void k_quant_given_scale(const void* __restric
       }
     }
   }
-  m = wave_max(m);
-  if (lane == 0) partial[blockIdx.x * 4 + (threadIdx.x >> 6)] = m;
+  __shared__ float red[16];
+  m = block_max(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
 __global__ __launch_bounds__(256) void k_partials_to_slot(const float* __restrict__ partial, int npartial,
                                                            float* __restrict__ slot) {
   __shared__ float red[16];
-  float m = 0.0f;
-  for (int i = threadIdx.x; i < npartial; i += 256) m = fmaxf(m, partial[i]);
-  m = block_max(m, red);
+  const float m = block_max_of(partial, npartial, red);
   if (threadIdx.x == 0) *slot = m;
 }
 
@@ -292,14 +285,14 @@ static void quantize_delayed_t(const void* x, int64_t total, float* hist, int64_
   }
   const int64_t nch = total / 8;
   int64_t p = (nch + 2047) / 2048;   // 8 chunks of 8 elements per thread
-  if (p > kTensorPartials / 4) p = kTensorPartials / 4;   // one partial per wave
+  if (p > kTensorPartials / 4) p = kTensorPartials / 4;   // grid-stride beyond that
   if (len > kFoldLen)
     hipLaunchKernelGGL((k_quant_given_scale<FMT, DT, false>), dim3((unsigned)p), dim3(256), 0, st, x, q, scale, hist,
                        len, margin, nch, partial);
   else
     hipLaunchKernelGGL((k_quant_given_scale<FMT, DT, true>), dim3((unsigned)p), dim3(256), 0, st, x, q, scale, hist,
                        len, margin, nch, partial);
-  hipLaunchKernelGGL(k_partials_to_slot, dim3(1), dim3(256), 0, st, partial, (int)(4 * p), hist + pos);
+  hipLaunchKernelGGL(k_partials_to_slot, dim3(1), dim3(256), 0, st, partial, (int)p, hist + pos);
 }
 
 hipError_t launch_quantize_delayed(const void* x, int dt, int64_t total, int fmt, float* hist, int64_t len,
