@@ -64,3 +64,32 @@ def test_delayed_scale_far_from_the_data(fmt):
         assert host(s).view(np.uint32)[0] == np.float32(want_s).view(np.uint32), (label, host(s), want_s)
         assert_codes_equal(host(q), want_q, label + " codes", x)
         assert np.array_equal(host(hist_d).view(np.uint32), want_h.view(np.uint32)), label
+
+
+@pytest.mark.parametrize("hlen", [1000, 4096, 4097, 10000])
+def test_delayed_long_history(hlen):
+    """Histories of up to 4096 entries are scanned by every wave of the encode
+    kernel; longer ones by a separate one-workgroup kernel.  Both reductions
+    keep several loads in flight per thread, with a tail for lengths that are
+    not a multiple of that stride: the maximum sits in the tail, NaN entries
+    are skipped, and the scale, codes and history must match the oracle bit
+    for bit."""
+    rng = np.random.default_rng(300 + hlen)
+    hist = rng.uniform(0.0, 5.0, hlen).astype(np.float32)
+    hist[rng.choice(hlen, 7, replace=False)] = np.float32(np.nan)
+    hist[hlen - 1] = np.float32(37.5)             # the maximum, in the last (tail) entry
+    pos = hlen // 3
+    fmt = fb.E4M3
+    x = (rng.standard_normal((64, 384)) * 4).astype(np.float32)
+    label = f"delayed long history len={hlen}"
+    say(label)
+    hist_d = dev(hist.copy())
+    q, s = fb.fp8_quantize_delayed(dev(x), fmt, hist_d, pos, 1)
+    torch.cuda.synchronize()
+    want_q, want_s, want_h = quant.quantize_delayed(x, hist, pos, 1, fmt)
+    assert host(s).view(np.uint32)[0] == np.float32(want_s).view(np.uint32), (label, host(s), want_s)
+    assert_codes_equal(host(q), want_q, label + " codes", x)
+    got_h = host(hist_d)
+    assert np.array_equal(np.isnan(got_h), np.isnan(want_h)), label
+    ok = ~np.isnan(want_h)
+    assert np.array_equal(got_h[ok].view(np.uint32), want_h[ok].view(np.uint32)), label
