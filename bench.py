@@ -62,6 +62,7 @@ import workloads  # noqa: E402
 METRIC = "block-scaled FP8 GEMM TFLOP/s (% fp8 MFMA peak); quantize GB/s (% HBM)"
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 matrix-core peak
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak
+PEAK_FP4_TFLOPS = 10100.0    # MI355X dense fp4 matrix-core peak
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E peak
 COPY_PROBE_BYTES = 256 << 20  # size of the plain copy that calibrates the byte counters
 
@@ -490,6 +491,9 @@ def bench_fp4(args, wl) -> int:
     gemm_tflops = flops / (gm_ms * 1e-3) / 1e12
     qbytes = lambda rows: rows * K * 2 + rows * K // 2 + rows * (K // blk)
     traffic = read_traffic(wl.name, "fp32")
+    # MXFP4 runs on the FP4 matrix cores (exact block sums); NVFP4 expands its
+    # codes times microscales to fp16 and runs on the fp16 ones.
+    peak = PEAK_FP4_TFLOPS if kind == fb.FP4_MX else PEAK_BF16_TFLOPS
     result = {
         "metric": "block-scaled FP4 GEMM TFLOP/s (exact products, fp32 sums); quantize GB/s",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
@@ -508,10 +512,12 @@ def bench_fp4(args, wl) -> int:
                                   "NVFP4 (E4M3 per 16 + fp32 tensor scale)") + ", bf16 out",
                    "step": "quantize X + quantize W + GEMM + dequantize X",
                    "rotated_input_sets": R,
-                   "accumulation": "codes times block scales expanded exactly to "
-                                   + ("bf16" if kind == fb.FP4_MX else "fp16") + ", matrix cores, fp32 sums"},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+                   "accumulation": ("FP4 matrix cores with UE8M0 block scales: exact 32-element block sums, "
+                                    "fp32 sums" if kind == fb.FP4_MX else
+                                    "codes times E4M3 microscales expanded exactly to fp16, fp16 matrix cores, "
+                                    "fp32 sums")},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4), "traffic": traffic},
         "kernels": {"gemm_ms": round(gm_ms, 4), "gemm_tflops": round(gemm_tflops, 1),
                     "quantize_x_ms": round(qx_ms, 4), "quantize_x_gbs": round(qbytes(M) / (qx_ms * 1e-3) / 1e9, 1),
                     "quantize_w_ms": round(qw_ms, 4), "quantize_w_gbs": round(qbytes(N) / (qw_ms * 1e-3) / 1e9, 1),

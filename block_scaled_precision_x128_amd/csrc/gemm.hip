@@ -39,6 +39,12 @@
 //   MODE_MX        32-element UE8M0 blocks: 2^(eA+eB) applied per 32-K block,
 //                  folded into the bf16 operands (exact path) or given to the
 //                  scaled MFMA (fast path)
+//   MODE_MX4       MXFP4 (E2M1 codes, UE8M0 per 32): the FP4 form of the
+//                  scaled MFMA, which sums each 32-element block exactly
+//                  (E2M1 products need at most 13 bits) and adds the block
+//                  sums in fp32, so it keeps the exact path's error bound
+//   MODE_NV4       NVFP4 (E2M1 codes, E4M3 microscale per 16, fp32 tensor
+//                  scales): codes times microscales expanded exactly to fp16
 #include <type_traits>
 
 #include "gemm_common.h"
@@ -93,7 +99,10 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   static_assert((TBM + TBN) % (8 * NW) == 0, "rows must split evenly over the waves");
   // FP4 operands: two codes per byte, so a K step of 128 bytes per row holds 256 K.
   constexpr bool FP4 = MODE == MODE_MX4 || MODE == MODE_NV4;
-  static_assert(!FP4 || PATH == PATH_EXACT, "FP4 operands take the exact path");
+  // MXFP4 runs on the FP4 matrix cores (PATH_FAST); NVFP4's E4M3 microscales
+  // are not powers of two, so its codes are expanded (PATH_EXACT).
+  static_assert(MODE != MODE_NV4 || PATH == PATH_EXACT, "NVFP4 operands take the exact path");
+  static_assert(MODE != MODE_MX4 || PATH == PATH_FAST, "MXFP4 operands take the FP4 matrix cores");
   // Scale words staged per row and step: FP8 MX 4 bytes (128 K / 32), MXFP4 8
   // bytes (256 K / 32), NVFP4 16 bytes (256 K / 16).
   constexpr int SW = MODE == MODE_MX4 ? 2 : (MODE == MODE_NV4 ? 4 : 1);
@@ -258,7 +267,36 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       }
     }
 
-    if constexpr (PATH == PATH_FAST) {
+    if constexpr (MODE == MODE_MX4) {
+      // MXFP4 on the FP4 matrix cores: a 256-K step is two 128-K halves, one
+      // instruction each.  In half h, lane group g holds chunk 4h + g of its
+      // row (K 128h + 32g .. +31, element 2i in the low nibble of byte i),
+      // which is exactly MX block 4h + g; its UE8M0 byte is byte g of staged
+      // scale word h.  The instruction scales each block's products by
+      // 2^(eA + eB) and sums every 32-element block exactly (E2M1 products
+      // span at most 13 bits), then adds the four block sums in fp32.
+      u32x4 bl[NJ], bh[NJ];
+      int eb0[NJ], eb1[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int r = b_row0 + 16 * j;
+        bl[j] = lds16(sb_, r * 128 + c0);
+        bh[j] = lds16(sb_, r * 128 + c1);
+        eb0[j] = (int)((s_e[buf][0][TBM + r] >> (8 * g)) & 0xffu);
+        eb1[j] = (int)((s_e[buf][1][TBM + r] >> (8 * g)) & 0xffu);
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int r = a_row0 + 16 * i;
+        const u32x4 al = lds16(sa_, r * 128 + c0), ah = lds16(sa_, r * 128 + c1);
+        const int ea0 = (int)((s_e[buf][0][r] >> (8 * g)) & 0xffu);
+        const int ea1 = (int)((s_e[buf][1][r] >> (8 * g)) & 0xffu);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_fp4(al, bl[j], acc[i][j], ea0, eb0[j]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_fp4(ah, bh[j], acc[i][j], ea1, eb1[j]);
+      }
+    } else if constexpr (PATH == PATH_FAST) {
       v8i fb[NJ];
       int eb[NJ] = {};
 #pragma unroll
@@ -290,40 +328,25 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
             acc[i][j] = mfma_fp8<AF, BF>(fa, fb[j], acc[i][j], (int)kUnitScale, (int)kUnitScale);
         }
       }
-    } else if constexpr (FP4) {
-      // FP4 exact path: the lane's two 16-byte chunks (2g, 2g+1) hold K
+    } else if constexpr (MODE == MODE_NV4) {
+      // NVFP4 exact path: the lane's two 16-byte chunks (2g, 2g+1) hold K
       // 64g..64g+63 of this 256-K step; each chunk is 32 codes, four matrix
       // operands of 8 (byte i of a word holds codes 2i, 2i+1 in its low and
-      // high nibble).  Every code times its block scale is exact:
-      //   MX: bf16 operands, 2^e applied by the convert (block 2g+h of the
-      //       step, one per chunk);
-      //   NV: fp16 operands, the E4M3 microscale applied by a packed fp16
-      //       multiply (the scaled converts keep only a scale's exponent);
-      //       words 0-1 and 2-3 of a chunk are blocks 4g+2h and 4g+2h+1,
-      //       bytes 2h and 2h+1 of staged word g.
-      using Op = typename std::conditional<MODE == MODE_NV4, v8h, v8bf>::type;
+      // high nibble).  Every code times its E4M3 microscale is exact in fp16,
+      // applied by a packed fp16 multiply (the scaled converts keep only a
+      // scale's exponent); words 0-1 and 2-3 of a chunk are blocks 4g+2h and
+      // 4g+2h+1, bytes 2h and 2h+1 of staged word g.
+      using Op = v8h;
       auto frag = [&](const uint8_t* base, int row, int R, int h, Op* x) {
         const u32x4 d = lds16(base, row * 128 + (h ? c1 : c0));
-        if constexpr (MODE == MODE_MX4) {
-          const int bi = 2 * g + h;
-          const float sc = e8m0_to_f32((s_e[buf][bi >> 2][R] >> (8 * (bi & 3))) & 0xffu);
-          x[0] = cvt8_fp4(d.x, sc);
-          x[1] = cvt8_fp4(d.y, sc);
-          x[2] = cvt8_fp4(d.z, sc);
-          x[3] = cvt8_fp4(d.w, sc);
-        } else {
-          const v2f m = h ? decode2<FMT_E4M3>(s_e[buf][g][R], true) : decode2<FMT_E4M3>(s_e[buf][g][R], false);
-          const v2h m0 = {(_Float16)m.x, (_Float16)m.x}, m1 = {(_Float16)m.y, (_Float16)m.y};
-          x[0] = cvt8_fp4_f16(d.x, m0);
-          x[1] = cvt8_fp4_f16(d.y, m0);
-          x[2] = cvt8_fp4_f16(d.z, m1);
-          x[3] = cvt8_fp4_f16(d.w, m1);
-        }
+        const v2f m = h ? decode2<FMT_E4M3>(s_e[buf][g][R], true) : decode2<FMT_E4M3>(s_e[buf][g][R], false);
+        const v2h m0 = {(_Float16)m.x, (_Float16)m.x}, m1 = {(_Float16)m.y, (_Float16)m.y};
+        x[0] = cvt8_fp4_f16(d.x, m0);
+        x[1] = cvt8_fp4_f16(d.y, m0);
+        x[2] = cvt8_fp4_f16(d.z, m1);
+        x[3] = cvt8_fp4_f16(d.w, m1);
       };
-      auto mma = [](const Op& a, const Op& b, const v4f& c) {
-        if constexpr (MODE == MODE_NV4) return mfma_f16(a, b, c);
-        else return mfma_bf16(a, b, c);
-      };
+      auto mma = [](const Op& a, const Op& b, const v4f& c) { return mfma_f16(a, b, c); };
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         Op xb[NJ][4];
@@ -628,8 +651,8 @@ static void tiled_mode(const GemmArgs& p, int mode, int odt, int path, hipStream
 hipError_t launch_gemm_fp4(const GemmArgs& p, int mode, int odt, hipStream_t st) {
   // the format template arguments are unused by the FP4 modes
   if (mode == MODE_MX4) {
-    if (odt == DT_F32) tiled_shape<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_F32, PATH_EXACT>(p, st);
-    else tiled_shape<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_BF16, PATH_EXACT>(p, st);
+    if (odt == DT_F32) tiled_shape<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_F32, PATH_FAST>(p, st);
+    else tiled_shape<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_BF16, PATH_FAST>(p, st);
   } else {
     if (odt == DT_F32) tiled_shape<FMT_E4M3, FMT_E4M3, MODE_NV4, DT_F32, PATH_EXACT>(p, st);
     else tiled_shape<FMT_E4M3, FMT_E4M3, MODE_NV4, DT_BF16, PATH_EXACT>(p, st);

@@ -77,6 +77,14 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, sa, 0, sb);
 }
 
+// FP4 (E2M1) x FP4 with UE8M0 block scales: each operand is 16 bytes (32
+// codes) per lane; the upper half of the 8-register operand is not read.
+__device__ __forceinline__ v4f mfma_fp4(const u32x4& a, const u32x4& b, const v4f& c, int sa, int sb) {
+  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, sa, 0, sb);
+}
+
 __device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -100,18 +108,6 @@ __device__ __forceinline__ v2bf cvt2(uint32_t w, float scale, bool hi) {
   }
 }
 
-// The 8 codes of dwords (d0, d1) -> one K=32 bf16 operand.
-// Eight E2M1 codes (one word, code 2i in the low nibble of byte i) to bf16,
-// times `scale`, a power of two: the scaled converts apply the exponent of
-// their scale operand only (measured), which is exact for 2^e in bf16's range.
-__device__ __forceinline__ v8bf cvt8_fp4(uint32_t w, float scale) {
-  const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
-  const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
-  const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
-  const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
-  return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
 // Eight E2M1 codes to fp16, times an E4M3 microscale m (given as the fp16
 // pair {m, m}): exact converts (scale 1) and a packed fp16 multiply, exact too
 // since a code times an E4M3 value has at most 6 significant bits and lies in
@@ -124,6 +120,7 @@ __device__ __forceinline__ v8h cvt8_fp4_f16(uint32_t w, v2h m) {
   return v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// The 8 codes of dwords (d0, d1) -> one K=32 bf16 operand.
 template <int FMT>
 __device__ __forceinline__ v8bf cvt8(uint32_t d0, uint32_t d1, float scale) {
   const v2bf p0 = cvt2<FMT>(d0, scale, false), p1 = cvt2<FMT>(d0, scale, true);
