@@ -338,11 +338,13 @@ fp8_status_t fp4_dequantize(const uint8_t* q, const uint8_t* block_scales, const
  *                 [N, K/16]; tensor scales a_tensor_scale, b_tensor_scale)
  * ("Illustrated GPU kernels, Part 8", "Low precision: FP8, FP4, and
  * microscaling": the scale factors travel with the data into the matrix
- * multiply.)  Products are formed exactly (each code times its block scale is
- * exact in bf16) and summed in fp32 on the bf16 matrix cores; the NV tensor
- * scales multiply the fp32 result.  Meets |out - exact| <= 1e-4 sum_k |deq
- * products| (plus half a bf16 ulp for bf16 output) while every code times its
- * scale stays inside bf16's range (MX exponents below 127).
+ * multiply.)  MX runs on the FP4 matrix cores: each 32-element block's
+ * products are summed exactly, scaled by 2^(ea + eb), and the block sums are
+ * added in fp32.  NV expands each code times its microscale exactly to fp16,
+ * sums in fp32 on the fp16 matrix cores, and multiplies the result by the
+ * tensor scales.  Meets |out - exact| <= 1e-4 sum_k |deq products| (plus half
+ * a bf16 ulp for bf16 output) while the scaled products stay inside fp32's
+ * range.
  * Shapes: M % 16 == 0, N % 16 == 0, K % 256 == 0, K <= 2^22.  a, b, out
  * 16-byte aligned; scale arrays 4-byte aligned.  out_dt FP8_DT_F32 or
  * FP8_DT_BF16.  K == 0 writes zeros. */
