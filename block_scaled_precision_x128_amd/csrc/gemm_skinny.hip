@@ -35,14 +35,17 @@
 namespace fp8blk {
 
 // LDS footprint of one wave's stage (bytes): W rows, X rows, then scales.
+// A step is 128 bytes of every row: 128 K of FP8 codes, 256 K of FP4 codes.
+// Scale words per step: MX one per row (4 UE8M0 bytes), MXFP4 two.
 template <int MODE, int MT, int T>
 struct SkinnyStage {
-  static constexpr int kW = 16 * T * 128;          // W tile rows (128 K bytes each)
+  static constexpr int kW = 16 * T * 128;          // W tile rows (128 bytes each)
   static constexpr int kX = 16 * MT * 128;         // X tile rows
-  static constexpr int kScale = MODE == MODE_PROMOTE ? 2 * 256 : (MODE == MODE_MX ? 3 * 256 : 0);
+  static constexpr int kScaleLoads = MODE == MODE_PROMOTE ? 2 : (MODE == MODE_MX ? 3 : (MODE == MODE_MX4 ? 6 : 0));
+  static constexpr int kScale = kScaleLoads * 256;
   static constexpr int kBytes = kW + kX + kScale;
   // loads issued per step (every one is issued, out-of-range ones read zeros)
-  static constexpr int kLoads = 2 * T + 2 * MT + (MODE == MODE_PROMOTE ? 2 : (MODE == MODE_MX ? 3 : 0));
+  static constexpr int kLoads = 2 * T + 2 * MT + kScaleLoads;
 };
 
 // R (W rows per workgroup) <= 16 * T <= 112, so a workgroup's rows touch at
@@ -55,14 +58,17 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
   static_assert(MT * T * 64 * 16 <= NS * St::kBytes, "partial tiles must fit in the wave's stages");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[S][NS][St::kBytes];
 
-  const int64_t M = p.M, N = p.N, K = p.K;
+  const int64_t M = p.M, N = p.N;
+  constexpr bool FP4 = MODE == MODE_MX4;
+  static_assert(!FP4 || PATH == PATH_FAST, "MXFP4 runs on the FP4 matrix cores");
+  const int64_t K = FP4 ? p.K / 2 : p.K;   // bytes per operand row
   const int64_t n0 = (int64_t)blockIdx.x * R;
   if (n0 >= N) return;  // whole workgroup: no barrier has been reached
   const int nkb = (int)(K / 128);
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), g = lane >> 4;
   const int kb0 = (int)((int64_t)w * nkb / S), kb1 = (int)((int64_t)(w + 1) * nkb / S);
   const int64_t rows = (N - n0) < R ? (N - n0) : R;
-  const int64_t kq = K / 32;
+  const int64_t kq = p.K / 32;   // MX scale bytes per row
 
   // Loads into LDS, 8 full 128-byte rows per instruction: lane q takes row
   // q/8 of its 8-row block and stored chunk q%8, i.e. logical chunk
@@ -81,8 +87,8 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
     rs_sx = rsrc(sxa, M * nkb * 4);                                    // sA[m, kb], lanes m < M
     rs_sw = rsrc(swb + blo * nkb, ((blo + 1 < nblk) ? 2 : 1) * nkb * 4);  // sB[blo + l, kb], l < 2
   }
-  if constexpr (MODE == MODE_MX) {
-    rs_ex = rsrc(p.sa, M * kq);                                        // 4 UE8M0 bytes of row m, step kb
+  if constexpr (MODE == MODE_MX || MODE == MODE_MX4) {
+    rs_ex = rsrc(p.sa, M * kq);                                        // UE8M0 bytes of row m, step kb
     rs_ew = rsrc(reinterpret_cast<const uint8_t*>(p.sb) + n0 * kq, rows * kq);
   }
 
@@ -112,6 +118,17 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
       dma_to_lds<4>(rs_ex, lds_addr(sc), lane * (int)kq + ks);
       dma_to_lds<4>(rs_ew, lds_addr(sc + 256), lane * (int)kq + ks);
       dma_to_lds<4>(rs_ew, lds_addr(sc + 512), (64 + lane) * (int)kq + ks);
+    }
+    if constexpr (MODE == MODE_MX4) {
+      // word wd (UE8M0 bytes 4wd .. 4wd+3 of the step) of X rows at sc + 256 wd,
+      // of W rows r < 128 at sc + 512 + 512 wd + 4 r
+      const int ks = valid ? k * 8 : kOutOfRange;
+#pragma unroll
+      for (int wd = 0; wd < 2; ++wd) {
+        dma_to_lds<4>(rs_ex, lds_addr(sc + 256 * wd), lane * (int)kq + ks + 4 * wd);
+        dma_to_lds<4>(rs_ew, lds_addr(sc + 512 + 512 * wd), lane * (int)kq + ks + 4 * wd);
+        dma_to_lds<4>(rs_ew, lds_addr(sc + 768 + 512 * wd), (64 + lane) * (int)kq + ks + 4 * wd);
+      }
     }
   };
 
@@ -160,7 +177,35 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
       for (int t = 0; t < T; ++t)
         eb[t] = (reinterpret_cast<const uint32_t*>(sc + 256)[16 * t + (lane & 15)] >> (8 * g)) & 0xffu;
     }
-    if constexpr (PATH == PATH_FAST) {
+    if constexpr (MODE == MODE_MX4) {
+      // Two FP4 instructions per step: half h takes chunk 4h + g of each row
+      // (K 128h + 32g .. +31), which is MX block 4h + g, scaled by byte g of
+      // the row's scale word h.
+      const uint32_t* sw32 = reinterpret_cast<const uint32_t*>(sc);
+      u32x4 al[MT], ah[MT];
+      int ea0[MT], ea1[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = St::kW + 16 * mt * 128 + rlane;
+        al[mt] = lds16(st, r + c0);
+        ah[mt] = lds16(st, r + c1);
+        ea0[mt] = (int)((sw32[16 * mt + (lane & 15)] >> (8 * g)) & 0xffu);
+        ea1[mt] = (int)((sw32[64 + 16 * mt + (lane & 15)] >> (8 * g)) & 0xffu);
+      }
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int r = 16 * t * 128 + rlane;
+        const u32x4 bl = lds16(st, r + c0), bh = lds16(st, r + c1);
+        const int wr = 16 * t + (lane & 15);
+        const int eb0 = (int)((sw32[128 + wr] >> (8 * g)) & 0xffu);
+        const int eb1 = (int)((sw32[256 + wr] >> (8 * g)) & 0xffu);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[mt][t] = mfma_fp4(al[mt], bl, acc[mt][t], ea0[mt], eb0);
+          acc[mt][t] = mfma_fp4(ah[mt], bh, acc[mt][t], ea1[mt], eb1);
+        }
+      }
+    } else if constexpr (PATH == PATH_FAST) {
       v8i fa[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -321,6 +366,13 @@ static void skinny_mode(const GemmArgs& p, int mode, int odt, int path, hipStrea
   if (mode == MODE_EPILOGUE) skinny_odt<AF, BF, MODE_EPILOGUE>(p, odt, path, st);
   else if (mode == MODE_PROMOTE) skinny_odt<AF, BF, MODE_PROMOTE>(p, odt, path, st);
   else skinny_odt<AF, BF, MODE_MX>(p, odt, path, st);
+}
+
+// MXFP4 operands (K % 256 == 0) on the FP4 matrix cores.
+hipError_t launch_gemm_skinny_fp4(const GemmArgs& p, int odt, hipStream_t st) {
+  if (odt == DT_F32) skinny_mt<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_F32, PATH_FAST>(p, st);
+  else skinny_mt<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_BF16, PATH_FAST>(p, st);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_skinny(const GemmArgs& p, int afmt, int bfmt, int mode, int odt, int path, hipStream_t st) {

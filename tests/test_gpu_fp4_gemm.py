@@ -91,3 +91,20 @@ def test_fp4_gemm_k_zero():
     fb.fp4_gemm_blockscaled(a, s, None, b, s[:0], None, fb.FP4_MX, fb.DT_F32, out=out)
     torch.cuda.synchronize()
     assert not host(out).any()
+
+
+@pytest.mark.parametrize("out_dt", [fb.DT_F32, fb.DT_BF16])
+@pytest.mark.parametrize("shape", [(16, 18432, 1024), (48, 784, 2048), (64, 5008, 1536),
+                                   (16, 48, 7168)])
+def test_mxfp4_gemm_decode_shapes(out_dt, shape):
+    """MXFP4 with M <= 64 runs the skinny kernel on the FP4 matrix cores:
+    workgroups own ceil(N / grid) weight rows (72 at N = 18432, not a whole
+    number of 16-row tiles; 20 at N = 5008), the waves split K, and X rows
+    past M read zeros.  Every output is checked."""
+    M, N, K = shape
+    label = f"mxfp4 decode gemm out={out_dt} shape={shape}"
+    say(label)
+    ops = _operands(fb.FP4_MX, M, N, K, 1700 + M + N + K)
+    out = _run(fb.FP4_MX, ops, out_dt)
+    ref, absb = fp4.gemm_ref(fb.FP4_MX, ops[0], ops[1], ops[3], ops[4], ops[2], ops[5])
+    gemm_check(out, out_dt, ref, absb, label)
