@@ -31,16 +31,17 @@ __device__ __forceinline__ void fp4_load8(const void* __restrict__ x, int64_t e0
   }
 }
 
-// E2M1 code of a finite fp32 value: round to nearest, ties to the even code,
-// saturating at 6, sign kept.  The magnitude code counts the rounding
-// boundaries at or below |q|; a boundary that is a tie counts only when the
-// code above it is the even one (0.75 -> 1.0, 1.75 -> 2, 3.5 -> 4), and is
-// passed strictly otherwise (0.25 -> 0, 1.25 -> 1.0, 2.5 -> 2, 5 -> 4).
-__device__ __forceinline__ uint32_t e2m1_code(float q) {
-  const float a = fabsf(q);
-  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-  return c | ((__float_as_uint(q) >> 28) & 8u);
+// Eight finite fp32 values to eight E2M1 codes, value i in nibble i (the low
+// nibble of byte i/2 for even i): the hardware convert, with a unit scale,
+// rounds to the nearest code with ties to the even one, saturates at 6 and
+// keeps the sign (negative values that round to zero give -0, code 8).
+__device__ __forceinline__ uint32_t e2m1_pack8(const float* q) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[0], q[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], 1.0f, 3);
+  return w;
 }
 
 // Smallest e with amax <= 6 * 2^e, clamped to [-127, 127]; -127 for 0.
@@ -73,10 +74,10 @@ __global__ __launch_bounds__(256) void k_fp4_quant_mx(const void* __restrict__ x
   fp4_load8<DT>(x, 8 * idx, v);
   const float m = group_max<4>(local_amax<8>(v));
   const int e = e2m1_mx_exponent(m);
-  uint32_t w = 0;
+  float sv[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) w |= e2m1_code(__builtin_amdgcn_ldexpf(v[i], -e)) << (4 * i);
-  *reinterpret_cast<uint32_t*>(q + 4 * idx) = w;
+  for (int i = 0; i < 8; ++i) sv[i] = __builtin_amdgcn_ldexpf(v[i], -e);   // exact: a power of two
+  *reinterpret_cast<uint32_t*>(q + 4 * idx) = e2m1_pack8(sv);
   if ((idx & 3) == 0) bs[idx >> 2] = (uint8_t)(e + 127);
 }
 
@@ -122,8 +123,10 @@ __global__ __launch_bounds__(256) void k_fp4_quant_nv(const void* __restrict__ x
     uint32_t w = 0;
     if (S != 0.0f) {
       const GivenScale g = given_scale(S);
+      float qv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w |= e2m1_code(quot_given(v[i], g)) << (4 * i);
+      for (int i = 0; i < 8; ++i) qv[i] = quot_given(v[i], g);
+      w = e2m1_pack8(qv);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) w |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * i);

@@ -127,3 +127,26 @@ def test_fp4_round_trip_full_width(kind):
     wq, wbs, wts = _oracle_quantize(kind, workloads.bf16_bits_to_f32(x))
     want = fp4.dequantize_mx(wq, wbs) if kind == fb.FP4_MX else fp4.dequantize_nv(wq, wbs, wts)
     assert_codes_equal(host(y).view(np.uint32), want.view(np.uint32), "fp4 round trip")
+
+
+@pytest.mark.parametrize("dt", [fb.DT_F32, fb.DT_BF16])
+def test_fp4_mx_every_bf16_value(dt):
+    """The E2M1 cast on every bf16 value of magnitude at most 6 (both signs,
+    zeros and bf16 subnormals included): each sits in an MX block whose first
+    element is 6, so the block exponent is 0 and the codes are the unscaled
+    cast.  The fp32 input also carries fp32 subnormals, which must round to
+    signed zeros."""
+    bits = np.arange(0, 0x10000, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 6.0)]
+    if dt == fb.DT_F32:
+        vals = np.concatenate([vals, np.array([1e-40, -1e-40, 1.4e-45, -1.4e-45, -3e-39], np.float32)])
+    per_block = 31
+    nblk = -(-vals.size // per_block)
+    nblk += (-nblk) % 4                       # rows of 128 elements (4 blocks)
+    x = np.zeros((nblk, 32), np.float32)
+    x[:, 0] = 6.0
+    flat = np.zeros(nblk * per_block, np.float32)
+    flat[:vals.size] = vals
+    x[:, 1:] = flat.reshape(nblk, per_block)
+    _check_quantize(fb.FP4_MX, dt, x.reshape(nblk // 4, 128), f"fp4 MX every bf16 value dt={dt}")
