@@ -108,3 +108,37 @@ def test_mxfp4_gemm_decode_shapes(out_dt, shape):
     out = _run(fb.FP4_MX, ops, out_dt)
     ref, absb = fp4.gemm_ref(fb.FP4_MX, ops[0], ops[1], ops[3], ops[4], ops[2], ops[5])
     gemm_check(out, out_dt, ref, absb, label)
+
+
+def _crafted_mx(rows, K, rng):
+    """E2M1 codes (two per byte, element 2i in the low nibble) whose 32-element
+    blocks each hold one +-6 among +-0.5s, or a +-6 that a -+6 cancels, and
+    UE8M0 scales spread over 2^-25 .. 2^25."""
+    codes = np.where(rng.random((rows, K)) < 0.5, 0x1, 0x9).astype(np.uint8)     # +-0.5
+    blk = codes.reshape(rows, K // 32, 32)
+    blk[:, :, 0] = np.where(rng.random((rows, K // 32)) < 0.5, 0x7, 0xF)          # +-6
+    cancel = rng.random((rows, K // 32)) < 0.3
+    blk[:, :, 1] = np.where(cancel, blk[:, :, 0] ^ 0x8, blk[:, :, 1])             # -+6 in some blocks
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    scales = rng.integers(127 - 25, 127 + 26, (rows, K // 32)).astype(np.uint8)
+    return packed, scales
+
+
+@pytest.mark.parametrize("M", [16, 128])
+def test_mxfp4_gemm_block_sums_exact(M):
+    """The FP4 matrix cores on the widest in-block mix of E2M1 products (36
+    against 0.25, and +-36 cancelling) with block scales over 2^-25 .. 2^25:
+    every E2M1 block sum spans at most 13 bits, so it is formed exactly, and
+    the scaled block sums and the K/128 instruction results are added in fp32.
+    The result must stay within 1e-5 sum_k |x w|, ten times inside the
+    contract's 1e-4 and above the worst case of those fp32 additions at
+    K = 2048.  M = 16 runs the skinny kernel, M = 128 the tiled one."""
+    rng = np.random.default_rng(4242 + M)
+    N, K = 256, 2048
+    a, sa = _crafted_mx(M, K, rng)
+    b, sb = _crafted_mx(N, K, rng)
+    label = f"mxfp4 crafted blocks M={M}"
+    say(label)
+    out = _run(fb.FP4_MX, (a, sa, None, b, sb, None), fb.DT_F32)
+    ref, absb = fp4.gemm_ref(fb.FP4_MX, a, sa, b, sb)
+    gemm_check(out, fb.DT_F32, ref, absb, label, rel=1e-5)
