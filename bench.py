@@ -422,6 +422,14 @@ def fp4_cpu_baseline(wl, x_rows: int, w_rows: int):
                       f"{dt:.2f} s"}
 
 
+def fp4_gemm_bytes(wl) -> int:
+    """Algorithmic bytes of one FP4 GEMM: both operands' codes (half a byte
+    per element) and block scales (one byte per 32 (MX) or 16 (NV) elements)
+    read once, the bf16 output written once."""
+    blk = 32 if wl.fp4_kind == workloads.FP4_MX else 16
+    return (wl.M + wl.N) * (wl.K // 2 + wl.K // blk) + wl.M * wl.N * 2
+
+
 def bench_fp4(args, wl) -> int:
     import torch
     import block_scaled_precision_x128_amd as fb
@@ -504,8 +512,7 @@ def bench_fp4(args, wl) -> int:
     # codes times microscales to fp16 and runs on the fp16 ones.  Decode shapes
     # are bound by streaming the weights: algorithmic bytes against HBM.
     peak = PEAK_FP4_TFLOPS if kind == fb.FP4_MX else PEAK_BF16_TFLOPS
-    gemm_bytes = (M + N) * (K // 2 + K // blk) + M * N * 2
-    gemm_gbs = gemm_bytes / (gm_ms * 1e-3) / 1e9
+    gemm_gbs = fp4_gemm_bytes(wl) / (gm_ms * 1e-3) / 1e9
     if decode:
         roofline = {"bound": "hbm", "achieved": round(gemm_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(gemm_gbs / PEAK_HBM_GBS, 4), "traffic": traffic}

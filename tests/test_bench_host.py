@@ -34,6 +34,14 @@ def test_gemm_and_dequantize_bytes():
     assert bench.dequant_bytes(c3) == 4096 * 7168 * 3 + 4096 * 56 * 4
 
 
+def test_fp4_gemm_bytes():
+    dec = workloads.FP4_CONFIGS["fp4_mx_decode_16x18432x7168"]
+    # codes (K/2 bytes a row) + UE8M0 scales (K/32) of X and W, bf16 out
+    assert bench.fp4_gemm_bytes(dec) == (16 + 18432) * (3584 + 224) + 16 * 18432 * 2 == 70839808
+    nv = workloads.FP4_CONFIGS["fp4_nv_4096x7168x7168"]
+    assert bench.fp4_gemm_bytes(nv) == (4096 + 7168) * (3584 + 448) + 4096 * 7168 * 2
+
+
 def _csv(path, rows):
     with open(path, "w", newline="") as f:
         wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
