@@ -359,9 +359,10 @@ fp8_status_t fp4_gemm_blockscaled(const uint8_t* a, const uint8_t* a_scales, con
   p.K = K;
   p.ldo = N;
   // decode shapes (M <= 64) stream the weights through the skinny kernel, as
-  // the FP8 GEMM's automatic choice does; NVFP4 always runs the tiled kernel
-  if (kind == FP4_SCALE_MX && M <= 64) return hip_status(launch_gemm_skinny_fp4(p, (int)out_dt, stream));
-  return hip_status(launch_gemm_fp4(p, kind == FP4_SCALE_MX ? MODE_MX4 : MODE_NV4, (int)out_dt, stream));
+  // the FP8 GEMM's automatic choice does
+  const int mode = kind == FP4_SCALE_MX ? MODE_MX4 : MODE_NV4;
+  if (M <= 64) return hip_status(launch_gemm_skinny_fp4(p, mode, (int)out_dt, stream));
+  return hip_status(launch_gemm_fp4(p, mode, (int)out_dt, stream));
 }
 
 }  // extern "C"

@@ -36,12 +36,13 @@ namespace fp8blk {
 
 // LDS footprint of one wave's stage (bytes): W rows, X rows, then scales.
 // A step is 128 bytes of every row: 128 K of FP8 codes, 256 K of FP4 codes.
-// Scale words per step: MX one per row (4 UE8M0 bytes), MXFP4 two.
+// Scale words per step: MX one per row (4 UE8M0 bytes), MXFP4 two, NVFP4 four
+// (16 E4M3 microscales).
 template <int MODE, int MT, int T>
 struct SkinnyStage {
   static constexpr int kW = 16 * T * 128;          // W tile rows (128 bytes each)
   static constexpr int kX = 16 * MT * 128;         // X tile rows
-  static constexpr int kScaleLoads = MODE == MODE_PROMOTE ? 2 : (MODE == MODE_MX ? 3 : (MODE == MODE_MX4 ? 6 : 0));
+  static constexpr int kScaleLoads = MODE == MODE_PROMOTE ? 2 : (MODE == MODE_MX ? 3 : (MODE == MODE_MX4 ? 6 : (MODE == MODE_NV4 ? 12 : 0)));
   static constexpr int kScale = kScaleLoads * 256;
   static constexpr int kBytes = kW + kX + kScale;
   // loads issued per step (every one is issued, out-of-range ones read zeros)
@@ -59,8 +60,9 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[S][NS][St::kBytes];
 
   const int64_t M = p.M, N = p.N;
-  constexpr bool FP4 = MODE == MODE_MX4;
-  static_assert(!FP4 || PATH == PATH_FAST, "MXFP4 runs on the FP4 matrix cores");
+  constexpr bool FP4 = MODE == MODE_MX4 || MODE == MODE_NV4;
+  static_assert(MODE != MODE_MX4 || PATH == PATH_FAST, "MXFP4 runs on the FP4 matrix cores");
+  static_assert(MODE != MODE_NV4 || PATH == PATH_EXACT, "NVFP4 runs on exact fp16 expansions");
   const int64_t K = FP4 ? p.K / 2 : p.K;   // bytes per operand row
   const int64_t n0 = (int64_t)blockIdx.x * R;
   if (n0 >= N) return;  // whole workgroup: no barrier has been reached
@@ -68,7 +70,7 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), g = lane >> 4;
   const int kb0 = (int)((int64_t)w * nkb / S), kb1 = (int)((int64_t)(w + 1) * nkb / S);
   const int64_t rows = (N - n0) < R ? (N - n0) : R;
-  const int64_t kq = p.K / 32;   // MX scale bytes per row
+  const int64_t kq = MODE == MODE_NV4 ? p.K / 16 : p.K / 32;   // scale bytes per row
 
   // Loads into LDS, 8 full 128-byte rows per instruction: lane q takes row
   // q/8 of its 8-row block and stored chunk q%8, i.e. logical chunk
@@ -87,8 +89,8 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
     rs_sx = rsrc(sxa, M * nkb * 4);                                    // sA[m, kb], lanes m < M
     rs_sw = rsrc(swb + blo * nkb, ((blo + 1 < nblk) ? 2 : 1) * nkb * 4);  // sB[blo + l, kb], l < 2
   }
-  if constexpr (MODE == MODE_MX || MODE == MODE_MX4) {
-    rs_ex = rsrc(p.sa, M * kq);                                        // UE8M0 bytes of row m, step kb
+  if constexpr (MODE == MODE_MX || MODE == MODE_MX4 || MODE == MODE_NV4) {
+    rs_ex = rsrc(p.sa, M * kq);                                        // scale bytes of row m, step kb
     rs_ew = rsrc(reinterpret_cast<const uint8_t*>(p.sb) + n0 * kq, rows * kq);
   }
 
@@ -119,15 +121,16 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
       dma_to_lds<4>(rs_ew, lds_addr(sc + 256), lane * (int)kq + ks);
       dma_to_lds<4>(rs_ew, lds_addr(sc + 512), (64 + lane) * (int)kq + ks);
     }
-    if constexpr (MODE == MODE_MX4) {
-      // word wd (UE8M0 bytes 4wd .. 4wd+3 of the step) of X rows at sc + 256 wd,
-      // of W rows r < 128 at sc + 512 + 512 wd + 4 r
-      const int ks = valid ? k * 8 : kOutOfRange;
+    if constexpr (MODE == MODE_MX4 || MODE == MODE_NV4) {
+      // word wd (scale bytes 4wd .. 4wd+3 of the step) of X rows at sc + 256 wd,
+      // of W rows r < 128 at sc + 256 NWD + 512 wd + 4 r
+      constexpr int NWD = MODE == MODE_NV4 ? 4 : 2;
+      const int ks = valid ? k * 4 * NWD : kOutOfRange;
 #pragma unroll
-      for (int wd = 0; wd < 2; ++wd) {
+      for (int wd = 0; wd < NWD; ++wd) {
         dma_to_lds<4>(rs_ex, lds_addr(sc + 256 * wd), lane * (int)kq + ks + 4 * wd);
-        dma_to_lds<4>(rs_ew, lds_addr(sc + 512 + 512 * wd), lane * (int)kq + ks + 4 * wd);
-        dma_to_lds<4>(rs_ew, lds_addr(sc + 768 + 512 * wd), (64 + lane) * (int)kq + ks + 4 * wd);
+        dma_to_lds<4>(rs_ew, lds_addr(sc + 256 * NWD + 512 * wd), lane * (int)kq + ks + 4 * wd);
+        dma_to_lds<4>(rs_ew, lds_addr(sc + 256 * NWD + 256 + 512 * wd), (64 + lane) * (int)kq + ks + 4 * wd);
       }
     }
   };
@@ -203,6 +206,37 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
         for (int mt = 0; mt < MT; ++mt) {
           acc[mt][t] = mfma_fp4(al[mt], bl, acc[mt][t], ea0[mt], eb0);
           acc[mt][t] = mfma_fp4(ah[mt], bh, acc[mt][t], ea1[mt], eb1);
+        }
+      }
+    } else if constexpr (MODE == MODE_NV4) {
+      // NVFP4: the lane's chunks 2g and 2g+1 hold K 64g .. 64g+63 of the step,
+      // NV blocks 4g .. 4g+3; chunk h is four fp16 operands of 8 codes, each
+      // code times its E4M3 microscale (exact in fp16): words 0-1 of the chunk
+      // take byte 2h of the row's scale word g, words 2-3 byte 2h+1.
+      const uint32_t* sw32 = reinterpret_cast<const uint32_t*>(sc);
+      auto frag = [&](int off, uint32_t mw, int h, v8h* x) {
+        const u32x4 d = lds16(st, off + (h ? c1 : c0));
+        const v2f m = h ? decode2<FMT_E4M3>(mw, true) : decode2<FMT_E4M3>(mw, false);
+        const v2h m0 = {(_Float16)m.x, (_Float16)m.x}, m1 = {(_Float16)m.y, (_Float16)m.y};
+        x[0] = cvt8_fp4_f16(d.x, m0);
+        x[1] = cvt8_fp4_f16(d.y, m0);
+        x[2] = cvt8_fp4_f16(d.z, m1);
+        x[3] = cvt8_fp4_f16(d.w, m1);
+      };
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v8h xa[MT][4];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          frag(St::kW + 16 * mt * 128 + rlane, sw32[64 * g + 16 * mt + (lane & 15)], h, xa[mt]);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          v8h xb[4];
+          frag(16 * t * 128 + rlane, sw32[256 + 128 * g + 16 * t + (lane & 15)], h, xb);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) acc[mt][t] = mfma_f16(xa[mt][s4], xb[s4], acc[mt][t]);
         }
       }
     } else if constexpr (PATH == PATH_FAST) {
@@ -313,6 +347,7 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
       for (int s = 0; s < S; ++s) v += reinterpret_cast<const float*>(&lds[s][0][0])[(u * 64 + lane) * 4 + r];
       if (row >= M) continue;
       if constexpr (MODE == MODE_EPILOGUE) v = v * (sxa[p.a_per_row ? row : 0] * swb[p.b_per_row ? col : 0]);
+      if constexpr (MODE == MODE_NV4) v = v * (p.ta[0] * p.tb[0]);
       store_out<ODT>(p.out, row * p.ldo + col, v);
     }
   }
@@ -368,10 +403,27 @@ static void skinny_mode(const GemmArgs& p, int mode, int odt, int path, hipStrea
   else skinny_odt<AF, BF, MODE_MX>(p, odt, path, st);
 }
 
-// MXFP4 operands (K % 256 == 0) on the FP4 matrix cores.
-hipError_t launch_gemm_skinny_fp4(const GemmArgs& p, int odt, hipStream_t st) {
-  if (odt == DT_F32) skinny_mt<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_F32, PATH_FAST>(p, st);
-  else skinny_mt<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_BF16, PATH_FAST>(p, st);
+// FP4 operands (K % 256 == 0): MXFP4 on the FP4 matrix cores, NVFP4 on exact
+// fp16 expansions.  NVFP4 stages four scale words per row and step, so with
+// four X tiles (M > 32) a workgroup takes four column tiles to stay within the
+// 160 KiB of LDS.
+template <int ODT>
+static void skinny_nv(const GemmArgs& p, hipStream_t st) {
+  const int64_t mt = (p.M + 15) / 16;
+  if (mt <= 1) skinny_launch<FMT_E4M3, FMT_E4M3, MODE_NV4, ODT, PATH_EXACT, 1, 5>(p, st);
+  else if (mt <= 2) skinny_launch<FMT_E4M3, FMT_E4M3, MODE_NV4, ODT, PATH_EXACT, 2, 5>(p, st);
+  else skinny_launch<FMT_E4M3, FMT_E4M3, MODE_NV4, ODT, PATH_EXACT, 4, 4>(p, st);
+}
+
+hipError_t launch_gemm_skinny_fp4(const GemmArgs& p, int mode, int odt, hipStream_t st) {
+  if (mode == MODE_NV4) {
+    if (odt == DT_F32) skinny_nv<DT_F32>(p, st);
+    else skinny_nv<DT_BF16>(p, st);
+  } else if (odt == DT_F32) {
+    skinny_mt<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_F32, PATH_FAST>(p, st);
+  } else {
+    skinny_mt<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_BF16, PATH_FAST>(p, st);
+  }
   return hipGetLastError();
 }
 

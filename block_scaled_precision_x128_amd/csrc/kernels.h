@@ -50,8 +50,9 @@ hipError_t launch_gemm_tiled(const GemmArgs& p, int afmt, int bfmt, int mode, in
 hipError_t launch_gemm_skinny(const GemmArgs& p, int afmt, int bfmt, int mode, int odt, int path, hipStream_t st);
 // FP4 operands (mode MODE_MX4 or MODE_NV4, odt DT_F32 / DT_BF16, K % 256 == 0).
 hipError_t launch_gemm_fp4(const GemmArgs& p, int mode, int odt, hipStream_t st);
-// MXFP4 operands with M <= 64 (decode shapes): the skinny kernel.
-hipError_t launch_gemm_skinny_fp4(const GemmArgs& p, int odt, hipStream_t st);
+// FP4 operands with M <= 64 (decode shapes): the skinny kernel (mode
+// MODE_MX4 or MODE_NV4).
+hipError_t launch_gemm_skinny_fp4(const GemmArgs& p, int mode, int odt, hipStream_t st);
 hipError_t launch_fill_zero(void* out, int64_t bytes, hipStream_t st);     // bytes % 4 == 0, 4-byte aligned
 hipError_t launch_fill_f32(float* out, int64_t n, float v, hipStream_t st);
 

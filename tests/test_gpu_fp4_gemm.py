@@ -110,6 +110,22 @@ def test_mxfp4_gemm_decode_shapes(out_dt, shape):
     gemm_check(out, out_dt, ref, absb, label)
 
 
+@pytest.mark.parametrize("out_dt", [fb.DT_F32, fb.DT_BF16])
+@pytest.mark.parametrize("shape", [(16, 18432, 1024), (32, 784, 2048), (64, 5008, 1536), (48, 48, 7168)])
+def test_nvfp4_gemm_decode_shapes(out_dt, shape):
+    """NVFP4 with M <= 64 runs the skinny kernel on exact fp16 expansions:
+    four microscale words per row and step, one to four X tiles (four column
+    tiles per workgroup when M > 32), the tensor scales in the epilogue.
+    Every output is checked."""
+    M, N, K = shape
+    label = f"nvfp4 decode gemm out={out_dt} shape={shape}"
+    say(label)
+    ops = _operands(fb.FP4_NV, M, N, K, 2700 + M + N + K)
+    out = _run(fb.FP4_NV, ops, out_dt)
+    ref, absb = fp4.gemm_ref(fb.FP4_NV, ops[0], ops[1], ops[3], ops[4], ops[2], ops[5])
+    gemm_check(out, out_dt, ref, absb, label)
+
+
 def _crafted_mx(rows, K, rng):
     """E2M1 codes (two per byte, element 2i in the low nibble) whose 32-element
     blocks each hold one +-6 among +-0.5s, or a +-6 that a -+6 cancels, and
