@@ -349,8 +349,8 @@ def fp4_gemm_blockscaled(a, a_scales, a_tensor_scale, b, b_scales, b_tensor_scal
                          out_dtype: int = DT_F32, out=None, stream=None):
     """FP4 block-scaled GEMM of packed E2M1 operands a [M, K/2], b [N, K/2]
     (K-contiguous) with their block (and, NV, tensor) scales.  MXFP4 runs on
-    the FP4 matrix cores (the skinny kernel when M <= 64), NVFP4 on exact fp16
-    expansions.  Returns out [M, N]."""
+    the FP4 matrix cores, NVFP4 on exact fp16 expansions; M <= 64 takes the
+    skinny (decode) kernel.  Returns out [M, N]."""
     torch = _torch()
     M, half = a.shape
     N = b.shape[0]

@@ -342,7 +342,8 @@ fp8_status_t fp4_dequantize(const uint8_t* q, const uint8_t* block_scales, const
  * products are summed exactly, scaled by 2^(ea + eb), and the block sums are
  * added in fp32.  NV expands each code times its microscale exactly to fp16,
  * sums in fp32 on the fp16 matrix cores, and multiplies the result by the
- * tensor scales.  Meets |out - exact| <= 1e-4 sum_k |deq products| (plus half
+ * tensor scales.  M <= 64 (decode shapes) runs a kernel that streams b once.
+ * Meets |out - exact| <= 1e-4 sum_k |deq products| (plus half
  * a bf16 ulp for bf16 output) while the scaled products stay inside fp32's
  * range.
  * Shapes: M % 16 == 0, N % 16 == 0, K % 256 == 0, K <= 2^22.  a, b, out
