@@ -26,9 +26,10 @@ in setup, as a model's weights are, and a step is quantize X + GEMM.
 
 The FP4 workloads (--workload fp4_mx_4096x7168x7168 / fp4_nv_4096x7168x7168:
 the DeepSeek shape and inputs with E2M1 operands, MXFP4 or NVFP4 scales) run
-quantize X + quantize W + GEMM + dequantize X the same way.  The MXFP4 decode
-workload (--workload fp4_mx_decode_16x18432x7168: c4's shape and inputs)
-quantizes W in setup, like c4, and reports the GEMM against HBM.
+quantize X + quantize W + GEMM + dequantize X the same way.  The FP4 decode
+workloads (--workload fp4_mx_decode_16x18432x7168 / fp4_nv_decode_16x18432x7168:
+c4's shape and inputs) quantize W in setup, like c4, and report the GEMM
+against HBM.
 
 The FP8 KV-cache workload (--workload kv_llama8b_b32_ctx8k: 32 sequences of
 8192 tokens, 8 KV heads of 128, bf16 states, E4M3 codes with per-channel

@@ -38,6 +38,9 @@ def test_fp4_gemm_bytes():
     dec = workloads.FP4_CONFIGS["fp4_mx_decode_16x18432x7168"]
     # codes (K/2 bytes a row) + UE8M0 scales (K/32) of X and W, bf16 out
     assert bench.fp4_gemm_bytes(dec) == (16 + 18432) * (3584 + 224) + 16 * 18432 * 2 == 70839808
+    nvd = workloads.FP4_CONFIGS["fp4_nv_decode_16x18432x7168"]
+    # NV microscales: one E4M3 byte per 16 elements (the tensor scales are 8 bytes, not counted)
+    assert bench.fp4_gemm_bytes(nvd) == (16 + 18432) * (3584 + 448) + 16 * 18432 * 2
     nv = workloads.FP4_CONFIGS["fp4_nv_4096x7168x7168"]
     assert bench.fp4_gemm_bytes(nv) == (4096 + 7168) * (3584 + 448) + 4096 * 7168 * 2
 

@@ -115,10 +115,13 @@ FP4_CONFIGS = {
     "fp4_nv_4096x7168x7168": Workload(
         "fp4_nv_4096x7168x7168", 103, 4096, 7168, 7168, DT_BF16, E4M3, E4M3,
         GRAN_MX32, GRAN_MX32, DT_BF16, 0.005, 100.0, "normal", fp4_kind=FP4_NV),
-    # the decode shape and inputs of c4_decode_skinny with MXFP4 operands
+    # the decode shape and inputs of c4_decode_skinny with MXFP4 / NVFP4 operands
     "fp4_mx_decode_16x18432x7168": Workload(
         "fp4_mx_decode_16x18432x7168", 104, 16, 18432, 7168, DT_BF16, E4M3, E4M3,
         GRAN_MX32, GRAN_MX32, DT_BF16, 0.0, 1.0, "normal", fp4_kind=FP4_MX),
+    "fp4_nv_decode_16x18432x7168": Workload(
+        "fp4_nv_decode_16x18432x7168", 104, 16, 18432, 7168, DT_BF16, E4M3, E4M3,
+        GRAN_MX32, GRAN_MX32, DT_BF16, 0.0, 1.0, "normal", fp4_kind=FP4_NV),
 }
 
 
