@@ -37,13 +37,14 @@ namespace fp8blk {
 // LDS footprint of one wave's stage (bytes): W rows, X rows, then scales.
 // A step is 128 bytes of every row: 128 K of FP8 codes, 256 K of FP4 codes.
 // Scale words per step: MX one per row (4 UE8M0 bytes), MXFP4 two, NVFP4 four
-// (16 E4M3 microscales).
+// (16 E4M3 microscales, staged row by row: 16 bytes per row).
 template <int MODE, int MT, int T>
 struct SkinnyStage {
   static constexpr int kW = 16 * T * 128;          // W tile rows (128 bytes each)
   static constexpr int kX = 16 * MT * 128;         // X tile rows
-  static constexpr int kScaleLoads = MODE == MODE_PROMOTE ? 2 : (MODE == MODE_MX ? 3 : (MODE == MODE_MX4 ? 6 : (MODE == MODE_NV4 ? 12 : 0)));
-  static constexpr int kScale = kScaleLoads * 256;
+  static constexpr int kScaleLoads = MODE == MODE_PROMOTE ? 2 : (MODE == MODE_MX ? 3 : (MODE == MODE_MX4 ? 6 : (MODE == MODE_NV4 ? 3 : 0)));
+  // NVFP4 stages each row's 16 scale bytes of a step with one 16-byte load per 64 rows
+  static constexpr int kScale = kScaleLoads * (MODE == MODE_NV4 ? 1024 : 256);
   static constexpr int kBytes = kW + kX + kScale;
   // loads issued per step (every one is issued, out-of-range ones read zeros)
   static constexpr int kLoads = 2 * T + 2 * MT + kScaleLoads;
@@ -121,17 +122,25 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
       dma_to_lds<4>(rs_ew, lds_addr(sc + 256), lane * (int)kq + ks);
       dma_to_lds<4>(rs_ew, lds_addr(sc + 512), (64 + lane) * (int)kq + ks);
     }
-    if constexpr (MODE == MODE_MX4 || MODE == MODE_NV4) {
-      // word wd (scale bytes 4wd .. 4wd+3 of the step) of X rows at sc + 256 wd,
-      // of W rows r < 128 at sc + 256 NWD + 512 wd + 4 r
-      constexpr int NWD = MODE == MODE_NV4 ? 4 : 2;
-      const int ks = valid ? k * 4 * NWD : kOutOfRange;
+    if constexpr (MODE == MODE_MX4) {
+      // word wd (UE8M0 bytes 4wd .. 4wd+3 of the step) of X rows at sc + 256 wd,
+      // of W rows r < 128 at sc + 512 + 512 wd + 4 r
+      const int ks = valid ? k * 8 : kOutOfRange;
 #pragma unroll
-      for (int wd = 0; wd < NWD; ++wd) {
+      for (int wd = 0; wd < 2; ++wd) {
         dma_to_lds<4>(rs_ex, lds_addr(sc + 256 * wd), lane * (int)kq + ks + 4 * wd);
-        dma_to_lds<4>(rs_ew, lds_addr(sc + 256 * NWD + 512 * wd), lane * (int)kq + ks + 4 * wd);
-        dma_to_lds<4>(rs_ew, lds_addr(sc + 256 * NWD + 256 + 512 * wd), (64 + lane) * (int)kq + ks + 4 * wd);
+        dma_to_lds<4>(rs_ew, lds_addr(sc + 512 + 512 * wd), lane * (int)kq + ks + 4 * wd);
+        dma_to_lds<4>(rs_ew, lds_addr(sc + 768 + 512 * wd), (64 + lane) * (int)kq + ks + 4 * wd);
       }
+    }
+    if constexpr (MODE == MODE_NV4) {
+      // a row's 16 microscale bytes of the step in one 16-byte load (kq and
+      // the step offset are multiples of 16): X rows at sc + 16 r, W rows
+      // r < 128 at sc + 1024 + 16 r
+      const int ks = valid ? k * 16 : kOutOfRange;
+      dma_to_lds<16>(rs_ex, lds_addr(sc), lane * (int)kq + ks);
+      dma_to_lds<16>(rs_ew, lds_addr(sc + 1024), lane * (int)kq + ks);
+      dma_to_lds<16>(rs_ew, lds_addr(sc + 2048), (64 + lane) * (int)kq + ks);
     }
   };
 
@@ -228,11 +237,11 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
         v8h xa[MT][4];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          frag(St::kW + 16 * mt * 128 + rlane, sw32[64 * g + 16 * mt + (lane & 15)], h, xa[mt]);
+          frag(St::kW + 16 * mt * 128 + rlane, sw32[4 * (16 * mt + (lane & 15)) + g], h, xa[mt]);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
           v8h xb[4];
-          frag(16 * t * 128 + rlane, sw32[256 + 128 * g + 16 * t + (lane & 15)], h, xb);
+          frag(16 * t * 128 + rlane, sw32[256 + 4 * (16 * t + (lane & 15)) + g], h, xb);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
