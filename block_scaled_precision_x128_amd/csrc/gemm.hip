@@ -105,9 +105,12 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   static_assert(MODE != MODE_MX4 || PATH == PATH_FAST, "MXFP4 operands take the FP4 matrix cores");
   // Scale words staged per row and step: FP8 MX 4 bytes (128 K / 32), MXFP4 8
   // bytes (256 K / 32), NVFP4 16 bytes (256 K / 16).
+  // NVFP4 stages a row's 16 bytes with one 16-byte load (s_e then holds 4
+  // consecutive words per row); MX stages word by word.
   constexpr int SW = MODE == MODE_MX4 ? 2 : (MODE == MODE_NV4 ? 4 : 1);
   constexpr int SCALE_CHUNKS = MODE == MODE_PROMOTE ? TBM / 64 + 1
-                               : (MODE == MODE_MX || FP4 ? SW * (TBM + TBN) / 64 : 0);
+                               : (MODE == MODE_NV4 ? (TBM + TBN) / 64
+                                                   : (MODE == MODE_MX || FP4 ? SW * (TBM + TBN) / 64 : 0));
   constexpr int SC = (SCALE_CHUNKS + NW - 1) / NW;     // scale loads per wave per step
   constexpr int LOADS = LPW + SC;                      // loads per wave per step
   static_assert((NS - 1) * LOADS <= 63, "loads in flight must fit the vmcnt counter");
@@ -189,7 +192,21 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
           dma_to_lds<4>(rssw, lds_addr(&s_spare[0]), kOutOfRange);
       }
     }
-    if constexpr (MODE == MODE_MX || FP4) {
+    if constexpr (MODE == MODE_NV4) {
+      // one 16-byte load per 64 rows: row R's words at s_e[buf] + 4 R
+      constexpr int RC = (TBM + TBN) / 64;
+      uint32_t* se = &s_e[buf][0][0];
+#pragma unroll
+      for (int t2 = 0; t2 < SC; ++t2) {
+        const int c = w + NW * t2;
+        if (c >= RC)
+          dma_to_lds<4>(rssb, lds_addr(&s_spare[0]), kOutOfRange);
+        else if (c < TBM / 64)
+          dma_to_lds<16>(rssa, lds_addr(se + 4 * 64 * c), (int)((64 * c + lane) * kq + kb * 16));
+        else
+          dma_to_lds<16>(rssb, lds_addr(se + 4 * 64 * c), (int)((64 * c - TBM + lane) * kq + kb * 16));
+      }
+    } else if constexpr (MODE == MODE_MX || FP4) {
       constexpr int RC = (TBM + TBN) / 64;   // row chunks; word wd of every row chunk is a chunk of its own
 #pragma unroll
       for (int t2 = 0; t2 < SC; ++t2) {
@@ -339,7 +356,8 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       using Op = v8h;
       auto frag = [&](const uint8_t* base, int row, int R, int h, Op* x) {
         const u32x4 d = lds16(base, row * 128 + (h ? c1 : c0));
-        const v2f m = h ? decode2<FMT_E4M3>(s_e[buf][g][R], true) : decode2<FMT_E4M3>(s_e[buf][g][R], false);
+        const uint32_t mw = (&s_e[buf][0][0])[4 * R + g];
+        const v2f m = h ? decode2<FMT_E4M3>(mw, true) : decode2<FMT_E4M3>(mw, false);
         const v2h m0 = {(_Float16)m.x, (_Float16)m.x}, m1 = {(_Float16)m.y, (_Float16)m.y};
         x[0] = cvt8_fp4_f16(d.x, m0);
         x[1] = cvt8_fp4_f16(d.y, m0);
