@@ -51,6 +51,12 @@
 
 namespace fp8blk {
 
+// MXFP4 with an even number of 256-K steps: a row's UE8M0 bytes of steps 2p
+// and 2p+1 (16 bytes, 16-byte aligned since the row holds K/32 bytes, a
+// multiple of 16) are staged with one 16-byte load at step 2p into a
+// two-slot ring, halving the scale loads.  Otherwise as MODE_MX4.
+constexpr int MODE_MX4_PAIRS = 5;
+
 // ---------------------------------------------------------------------------
 // Tiled kernel: a workgroup of 8 waves (2 along M x 4 along N) computes a
 // 256x256 output tile (wave tiles 128x64; 256x192 and 128x256 variants
@@ -98,27 +104,31 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   constexpr int LPW = (TBM + TBN) / 8 / NW;            // 1-KiB loads per wave per K step
   static_assert((TBM + TBN) % (8 * NW) == 0, "rows must split evenly over the waves");
   // FP4 operands: two codes per byte, so a K step of 128 bytes per row holds 256 K.
-  constexpr bool FP4 = MODE == MODE_MX4 || MODE == MODE_NV4;
+  constexpr bool PAIRS = MODE == MODE_MX4_PAIRS;
+  constexpr bool MX4 = MODE == MODE_MX4 || PAIRS;
+  constexpr bool FP4 = MX4 || MODE == MODE_NV4;
   // MXFP4 runs on the FP4 matrix cores (PATH_FAST); NVFP4's E4M3 microscales
   // are not powers of two, so its codes are expanded (PATH_EXACT).
   static_assert(MODE != MODE_NV4 || PATH == PATH_EXACT, "NVFP4 operands take the exact path");
-  static_assert(MODE != MODE_MX4 || PATH == PATH_FAST, "MXFP4 operands take the FP4 matrix cores");
+  static_assert(!MX4 || PATH == PATH_FAST, "MXFP4 operands take the FP4 matrix cores");
   // Scale words staged per row and step: FP8 MX 4 bytes (128 K / 32), MXFP4 8
   // bytes (256 K / 32), NVFP4 16 bytes (256 K / 16).
   // NVFP4 stages a row's 16 bytes with one 16-byte load (s_e then holds 4
-  // consecutive words per row); MX stages word by word.
-  constexpr int SW = MODE == MODE_MX4 ? 2 : (MODE == MODE_NV4 ? 4 : 1);
+  // consecutive words per row), MODE_MX4_PAIRS two steps' 8 bytes the same
+  // way on even steps only; MX and MODE_MX4 stage word by word.
+  constexpr int SW = MODE == MODE_MX4 ? 2 : (MODE == MODE_NV4 || PAIRS ? 4 : 1);
   constexpr int SCALE_CHUNKS = MODE == MODE_PROMOTE ? TBM / 64 + 1
-                               : (MODE == MODE_NV4 ? (TBM + TBN) / 64
-                                                   : (MODE == MODE_MX || FP4 ? SW * (TBM + TBN) / 64 : 0));
-  constexpr int SC = (SCALE_CHUNKS + NW - 1) / NW;     // scale loads per wave per step
-  constexpr int LOADS = LPW + SC;                      // loads per wave per step
+                               : (MODE == MODE_NV4 || PAIRS ? (TBM + TBN) / 64
+                                                            : (MODE == MODE_MX || FP4 ? SW * (TBM + TBN) / 64 : 0));
+  constexpr int SC = (SCALE_CHUNKS + NW - 1) / NW;     // scale loads per wave per (even) step
+  constexpr int LOADS = LPW + SC;                      // loads per wave per step (MODE_MX4_PAIRS: even steps)
+  constexpr int ES = PAIRS ? 2 : NS;                   // scale stages
   static_assert((NS - 1) * LOADS <= 63, "loads in flight must fit the vmcnt counter");
   static_assert(TBM % 64 == 0 && (TBM + TBN) % 64 == 0, "scale loads move 64 rows at a time");
   // NS LDS stages; the loads of the next NS-1 K steps are in flight while one is computed.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS][(TBM + TBN) * TBK];
   __shared__ __attribute__((aligned(16))) float s_x[NS][TBM];                    // MODE_PROMOTE: sA[m, kb]
-  __shared__ __attribute__((aligned(16))) uint32_t s_e[NS][SW][TBM + TBN];       // MX / FP4: scale words per row
+  __shared__ __attribute__((aligned(16))) uint32_t s_e[ES][SW][TBM + TBN];       // MX / FP4: scale words per row
   __shared__ __attribute__((aligned(16))) float s_w[NS][64];                     // MODE_PROMOTE: sB[n/128, kb]
   __shared__ __attribute__((aligned(16))) uint32_t s_spare[64];                  // target of filler loads
 
@@ -192,19 +202,22 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
           dma_to_lds<4>(rssw, lds_addr(&s_spare[0]), kOutOfRange);
       }
     }
-    if constexpr (MODE == MODE_NV4) {
-      // one 16-byte load per 64 rows: row R's words at s_e[buf] + 4 R
+    if constexpr (MODE == MODE_NV4 || PAIRS) {
+      // one 16-byte load per 64 rows: row R's words at s_e[slot] + 4 R
+      // (MODE_MX4_PAIRS: steps kb, kb+1 into slot kb/2 % 2, at even kb only)
       constexpr int RC = (TBM + TBN) / 64;
-      uint32_t* se = &s_e[buf][0][0];
+      if (PAIRS && (kb & 1)) return;
+      uint32_t* se = &s_e[PAIRS ? (kb >> 1) & 1 : buf][0][0];
 #pragma unroll
       for (int t2 = 0; t2 < SC; ++t2) {
         const int c = w + NW * t2;
         if (c >= RC)
           dma_to_lds<4>(rssb, lds_addr(&s_spare[0]), kOutOfRange);
         else if (c < TBM / 64)
-          dma_to_lds<16>(rssa, lds_addr(se + 4 * 64 * c), (int)((64 * c + lane) * kq + kb * 16));
+          dma_to_lds<16>(rssa, lds_addr(se + 4 * 64 * c), (int)((64 * c + lane) * kq + kb * (PAIRS ? 8 : 16)));
         else
-          dma_to_lds<16>(rssb, lds_addr(se + 4 * 64 * c), (int)((64 * c - TBM + lane) * kq + kb * 16));
+          dma_to_lds<16>(rssb, lds_addr(se + 4 * 64 * c),
+                         (int)((64 * c - TBM + lane) * kq + kb * (PAIRS ? 8 : 16)));
       }
     } else if constexpr (MODE == MODE_MX || FP4) {
       constexpr int RC = (TBM + TBN) / 64;   // row chunks; word wd of every row chunk is a chunk of its own
@@ -260,8 +273,13 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
     // Wait for this step's loads; those of later steps stay in flight (every
     // wave issues LOADS per step, and loads complete in issue order).
     if constexpr (NS == 3) {
-      if (kb + 1 < nkb) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // (MODE_MX4_PAIRS: odd steps issue no scale loads)
+      if (kb + 1 < nkb) {
+        if (PAIRS && ((kb + 1) & 1)) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
     } else {
       static_assert(NS == 2, "two or three stages");
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -284,7 +302,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       }
     }
 
-    if constexpr (MODE == MODE_MX4) {
+    if constexpr (MX4) {
       // MXFP4 on the FP4 matrix cores: a 256-K step is two 128-K halves, one
       // instruction each.  In half h, lane group g holds chunk 4h + g of its
       // row (K 128h + 32g .. +31, element 2i in the low nibble of byte i),
@@ -292,6 +310,17 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       // scale word h.  The instruction scales each block's products by
       // 2^(eA + eB) and sums every 32-element block exactly (E2M1 products
       // span at most 13 bits), then adds the four block sums in fp32.
+      // Scale words (h = 0, 1) of row R: s_e[buf][h][R], or with
+      // MODE_MX4_PAIRS words 2 (kb & 1) + h of row R's four in its slot.
+      const uint32_t* sp = &s_e[(kb >> 1) & 1][0][0] + 2 * (kb & 1);
+      auto scale_words = [&](int row) {
+        if constexpr (PAIRS) {
+          const uint2 v = *reinterpret_cast<const uint2*>(sp + 4 * row);
+          return v;
+        } else {
+          return uint2{s_e[buf][0][row], s_e[buf][1][row]};
+        }
+      };
       u32x4 bl[NJ], bh[NJ];
       int eb0[NJ], eb1[NJ];
 #pragma unroll
@@ -299,15 +328,17 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         const int r = b_row0 + 16 * j;
         bl[j] = lds16(sb_, r * 128 + c0);
         bh[j] = lds16(sb_, r * 128 + c1);
-        eb0[j] = (int)((s_e[buf][0][TBM + r] >> (8 * g)) & 0xffu);
-        eb1[j] = (int)((s_e[buf][1][TBM + r] >> (8 * g)) & 0xffu);
+        const uint2 e = scale_words(TBM + r);
+        eb0[j] = (int)((e.x >> (8 * g)) & 0xffu);
+        eb1[j] = (int)((e.y >> (8 * g)) & 0xffu);
       }
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const int r = a_row0 + 16 * i;
         const u32x4 al = lds16(sa_, r * 128 + c0), ah = lds16(sa_, r * 128 + c1);
-        const int ea0 = (int)((s_e[buf][0][r] >> (8 * g)) & 0xffu);
-        const int ea1 = (int)((s_e[buf][1][r] >> (8 * g)) & 0xffu);
+        const uint2 e = scale_words(r);
+        const int ea0 = (int)((e.x >> (8 * g)) & 0xffu);
+        const int ea1 = (int)((e.y >> (8 * g)) & 0xffu);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_fp4(al, bl[j], acc[i][j], ea0, eb0[j]);
 #pragma unroll
@@ -601,12 +632,12 @@ hipError_t launch_fill_f32(float* out, int64_t n, float v, hipStream_t st) {
 // multiple of 128, so every scale layout splits at a block boundary).
 static GemmArgs column_range(const GemmArgs& p, int64_t c0, int64_t n, int mode, int odt) {
   GemmArgs q = p;
-  const bool fp4 = mode == MODE_MX4 || mode == MODE_NV4;
+  const bool fp4 = mode == MODE_MX4 || mode == MODE_MX4_PAIRS || mode == MODE_NV4;
   q.b = p.b + c0 * (fp4 ? p.K / 2 : p.K);
   q.N = n;
   q.out = static_cast<uint8_t*>(p.out) + c0 * (odt == DT_F32 ? 4 : 2);
   if (mode == MODE_PROMOTE) q.sb = static_cast<const float*>(p.sb) + (c0 / 128) * (p.K / 128);
-  else if (mode == MODE_MX || mode == MODE_MX4) q.sb = static_cast<const uint8_t*>(p.sb) + c0 * (p.K / 32);
+  else if (mode == MODE_MX || mode == MODE_MX4 || mode == MODE_MX4_PAIRS) q.sb = static_cast<const uint8_t*>(p.sb) + c0 * (p.K / 32);
   else if (mode == MODE_NV4) q.sb = static_cast<const uint8_t*>(p.sb) + c0 * (p.K / 16);
   else if (p.b_per_row) q.sb = static_cast<const float*>(p.sb) + c0;
   return q;
@@ -674,7 +705,10 @@ static void tiled_mode(const GemmArgs& p, int mode, int odt, int path, hipStream
 
 hipError_t launch_gemm_fp4(const GemmArgs& p, int mode, int odt, hipStream_t st) {
   // the format template arguments are unused by the FP4 modes
-  if (mode == MODE_MX4) {
+  if (mode == MODE_MX4 && (p.K / 256) % 2 == 0) {
+    if (odt == DT_F32) tiled_shape<FMT_E4M3, FMT_E4M3, MODE_MX4_PAIRS, DT_F32, PATH_FAST>(p, st);
+    else tiled_shape<FMT_E4M3, FMT_E4M3, MODE_MX4_PAIRS, DT_BF16, PATH_FAST>(p, st);
+  } else if (mode == MODE_MX4) {
     if (odt == DT_F32) tiled_shape<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_F32, PATH_FAST>(p, st);
     else tiled_shape<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_BF16, PATH_FAST>(p, st);
   } else {

@@ -71,14 +71,28 @@ def test_fp4_gemm_wide_scales(kind):
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("N", [4096, 4480])
 def test_fp4_gemm_large_tiles(kind, N):
-    """4096 x N x 256: 256x256 tiles (N = 4096) and the column split (N = 4480);
-    every output is checked."""
+    """4096 x N x 256: 256x256 tiles (N = 4096) and, with N = 4480, a ragged
+    last tile column (NVFP4: the column split); every output is checked."""
     M, K = 4096, 256
     label = f"fp4 gemm large kind={kind} shape={(M, N, K)}"
     say(label)
     ops = _operands(kind, M, N, K, 970 + kind + N)
     out = _run(kind, ops, fb.DT_BF16)
     ref, absb = fp4.gemm_ref(kind, ops[0], ops[1], ops[3], ops[4], ops[2], ops[5])
+    gemm_check(out, fb.DT_BF16, ref, absb, label)
+
+
+@pytest.mark.parametrize("K", [1024, 1280])
+def test_mxfp4_gemm_large_tiles_even_odd_steps(K):
+    """MXFP4 at 4096 x 4352 x K on 256x256 tiles: K = 1024 has an even number
+    of 256-K steps (two steps' scale bytes staged per load), K = 1280 an odd
+    one (word-by-word staging); every output is checked."""
+    M, N = 4096, 4352
+    label = f"mxfp4 gemm large shape={(M, N, K)}"
+    say(label)
+    ops = _operands(fb.FP4_MX, M, N, K, 990 + K)
+    out = _run(fb.FP4_MX, ops, fb.DT_BF16)
+    ref, absb = fp4.gemm_ref(fb.FP4_MX, ops[0], ops[1], ops[3], ops[4], ops[2], ops[5])
     gemm_check(out, fb.DT_BF16, ref, absb, label)
 
 
