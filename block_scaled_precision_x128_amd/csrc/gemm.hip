@@ -51,11 +51,10 @@
 
 namespace fp8blk {
 
-// MXFP4 with an even number of 256-K steps: a row's UE8M0 bytes of steps 2p
-// and 2p+1 (16 bytes, 16-byte aligned since the row holds K/32 bytes, a
-// multiple of 16) are staged with one 16-byte load at step 2p into a
+// MODE_MX4_PAIRS (an even number of 256-K steps): a row's UE8M0 bytes of
+// steps 2p and 2p+1 (16 bytes, 16-byte aligned since the row holds K/32
+// bytes, a multiple of 16) are staged with one 16-byte load at step 2p into a
 // two-slot ring, halving the scale loads.  Otherwise as MODE_MX4.
-constexpr int MODE_MX4_PAIRS = 5;
 
 // ---------------------------------------------------------------------------
 // Tiled kernel: a workgroup of 8 waves (2 along M x 4 along N) computes a

@@ -37,14 +37,18 @@ namespace fp8blk {
 // LDS footprint of one wave's stage (bytes): W rows, X rows, then scales.
 // A step is 128 bytes of every row: 128 K of FP8 codes, 256 K of FP4 codes.
 // Scale words per step: MX one per row (4 UE8M0 bytes), MXFP4 two, NVFP4 four
-// (16 E4M3 microscales, staged row by row: 16 bytes per row).
+// (16 E4M3 microscales, staged row by row: 16 bytes per row).  MODE_MX4_PAIRS
+// stages the 16-byte aligned block of a row's scale bytes that holds the
+// step's 8 (those of the step pair), also row by row.
 template <int MODE, int MT, int T>
 struct SkinnyStage {
   static constexpr int kW = 16 * T * 128;          // W tile rows (128 bytes each)
   static constexpr int kX = 16 * MT * 128;         // X tile rows
-  static constexpr int kScaleLoads = MODE == MODE_PROMOTE ? 2 : (MODE == MODE_MX ? 3 : (MODE == MODE_MX4 ? 6 : (MODE == MODE_NV4 ? 3 : 0)));
-  // NVFP4 stages each row's 16 scale bytes of a step with one 16-byte load per 64 rows
-  static constexpr int kScale = kScaleLoads * (MODE == MODE_NV4 ? 1024 : 256);
+  static constexpr bool kRow16 = MODE == MODE_NV4 || MODE == MODE_MX4_PAIRS;
+  static constexpr int kScaleLoads =
+      MODE == MODE_PROMOTE ? 2 : (MODE == MODE_MX ? 3 : (MODE == MODE_MX4 ? 6 : (kRow16 ? 3 : 0)));
+  // NVFP4 and MODE_MX4_PAIRS stage 16 scale bytes per row with one 16-byte load per 64 rows
+  static constexpr int kScale = kScaleLoads * (kRow16 ? 1024 : 256);
   static constexpr int kBytes = kW + kX + kScale;
   // loads issued per step (every one is issued, out-of-range ones read zeros)
   static constexpr int kLoads = 2 * T + 2 * MT + kScaleLoads;
@@ -61,8 +65,10 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[S][NS][St::kBytes];
 
   const int64_t M = p.M, N = p.N;
-  constexpr bool FP4 = MODE == MODE_MX4 || MODE == MODE_NV4;
-  static_assert(MODE != MODE_MX4 || PATH == PATH_FAST, "MXFP4 runs on the FP4 matrix cores");
+  constexpr bool PAIRS = MODE == MODE_MX4_PAIRS;
+  constexpr bool MX4 = MODE == MODE_MX4 || PAIRS;
+  constexpr bool FP4 = MX4 || MODE == MODE_NV4;
+  static_assert(!MX4 || PATH == PATH_FAST, "MXFP4 runs on the FP4 matrix cores");
   static_assert(MODE != MODE_NV4 || PATH == PATH_EXACT, "NVFP4 runs on exact fp16 expansions");
   const int64_t K = FP4 ? p.K / 2 : p.K;   // bytes per operand row
   const int64_t n0 = (int64_t)blockIdx.x * R;
@@ -90,7 +96,7 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
     rs_sx = rsrc(sxa, M * nkb * 4);                                    // sA[m, kb], lanes m < M
     rs_sw = rsrc(swb + blo * nkb, ((blo + 1 < nblk) ? 2 : 1) * nkb * 4);  // sB[blo + l, kb], l < 2
   }
-  if constexpr (MODE == MODE_MX || MODE == MODE_MX4 || MODE == MODE_NV4) {
+  if constexpr (MODE == MODE_MX || FP4) {
     rs_ex = rsrc(p.sa, M * kq);                                        // scale bytes of row m, step kb
     rs_ew = rsrc(reinterpret_cast<const uint8_t*>(p.sb) + n0 * kq, rows * kq);
   }
@@ -133,11 +139,12 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
         dma_to_lds<4>(rs_ew, lds_addr(sc + 768 + 512 * wd), (64 + lane) * (int)kq + ks + 4 * wd);
       }
     }
-    if constexpr (MODE == MODE_NV4) {
-      // a row's 16 microscale bytes of the step in one 16-byte load (kq and
-      // the step offset are multiples of 16): X rows at sc + 16 r, W rows
-      // r < 128 at sc + 1024 + 16 r
-      const int ks = valid ? k * 16 : kOutOfRange;
+    if constexpr (MODE == MODE_NV4 || PAIRS) {
+      // a row's 16 microscale bytes of the step (NVFP4), or the 16 scale
+      // bytes of the step pair (MODE_MX4_PAIRS), in one 16-byte load (kq and
+      // the offset are multiples of 16): X rows at sc + 16 r, W rows r < 128
+      // at sc + 1024 + 16 r
+      const int ks = valid ? (PAIRS ? (k & ~1) * 8 : k * 16) : kOutOfRange;
       dma_to_lds<16>(rs_ex, lds_addr(sc), lane * (int)kq + ks);
       dma_to_lds<16>(rs_ew, lds_addr(sc + 1024), lane * (int)kq + ks);
       dma_to_lds<16>(rs_ew, lds_addr(sc + 2048), (64 + lane) * (int)kq + ks);
@@ -162,7 +169,7 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
 
   auto lds16 = [&](const uint8_t* b, int off) { return *reinterpret_cast<const u32x4*>(b + off); };
 
-  auto compute = [&](int stage) {
+  auto compute = [&](int stage, int k) {
     const uint8_t* st = &lds[w][stage][0];
     const uint8_t* sc = st + St::kW + St::kX;
     float f_lo[MT][4], f_hi[MT][4];
@@ -189,11 +196,19 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
       for (int t = 0; t < T; ++t)
         eb[t] = (reinterpret_cast<const uint32_t*>(sc + 256)[16 * t + (lane & 15)] >> (8 * g)) & 0xffu;
     }
-    if constexpr (MODE == MODE_MX4) {
+    if constexpr (MX4) {
       // Two FP4 instructions per step: half h takes chunk 4h + g of each row
       // (K 128h + 32g .. +31), which is MX block 4h + g, scaled by byte g of
-      // the row's scale word h.
+      // the row's scale word h (MODE_MX4_PAIRS: word 2 (k & 1) + h of the
+      // row's four).
       const uint32_t* sw32 = reinterpret_cast<const uint32_t*>(sc);
+      auto words = [&](int xw, int row) {   // xw: 0 for X rows, 1 for W rows
+        if constexpr (PAIRS) {
+          return *reinterpret_cast<const uint2*>(sw32 + 256 * xw + 4 * row + 2 * (k & 1));
+        } else {
+          return uint2{sw32[128 * xw + row], sw32[64 + 192 * xw + row]};
+        }
+      };
       u32x4 al[MT], ah[MT];
       int ea0[MT], ea1[MT];
 #pragma unroll
@@ -201,16 +216,17 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
         const int r = St::kW + 16 * mt * 128 + rlane;
         al[mt] = lds16(st, r + c0);
         ah[mt] = lds16(st, r + c1);
-        ea0[mt] = (int)((sw32[16 * mt + (lane & 15)] >> (8 * g)) & 0xffu);
-        ea1[mt] = (int)((sw32[64 + 16 * mt + (lane & 15)] >> (8 * g)) & 0xffu);
+        const uint2 e = words(0, 16 * mt + (lane & 15));
+        ea0[mt] = (int)((e.x >> (8 * g)) & 0xffu);
+        ea1[mt] = (int)((e.y >> (8 * g)) & 0xffu);
       }
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const int r = 16 * t * 128 + rlane;
         const u32x4 bl = lds16(st, r + c0), bh = lds16(st, r + c1);
-        const int wr = 16 * t + (lane & 15);
-        const int eb0 = (int)((sw32[128 + wr] >> (8 * g)) & 0xffu);
-        const int eb1 = (int)((sw32[256 + wr] >> (8 * g)) & 0xffu);
+        const uint2 e = words(1, 16 * t + (lane & 15));
+        const int eb0 = (int)((e.x >> (8 * g)) & 0xffu);
+        const int eb1 = (int)((e.y >> (8 * g)) & 0xffu);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           acc[mt][t] = mfma_fp4(al[mt], bl, acc[mt][t], ea0[mt], eb0);
@@ -327,7 +343,7 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
     for (int k = kb0; k < kb1; ++k) {
       issue(k + NS - 1, cs == 0 ? NS - 1 : cs - 1);
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 1) * St::kLoads) : "memory");
-      compute(cs);
+      compute(cs, k);
       cs = cs + 1 == NS ? 0 : cs + 1;
     }
   }
@@ -424,14 +440,28 @@ static void skinny_nv(const GemmArgs& p, hipStream_t st) {
   else skinny_launch<FMT_E4M3, FMT_E4M3, MODE_NV4, ODT, PATH_EXACT, 4, 4>(p, st);
 }
 
+// MXFP4 with K % 512 == 0 and M <= 32 stages the scale bytes of step pairs
+// row by row (MODE_MX4_PAIRS); with four X tiles that stage would not fit
+// five column tiles in LDS, so M > 32 stages word by word.
+template <int ODT>
+static void skinny_mx4(const GemmArgs& p, hipStream_t st) {
+  const int64_t mt = (p.M + 15) / 16;
+  const bool pairs = p.K % 512 == 0;
+  if (mt <= 1 && pairs) skinny_launch<FMT_E4M3, FMT_E4M3, MODE_MX4_PAIRS, ODT, PATH_FAST, 1, 5>(p, st);
+  else if (mt <= 1) skinny_launch<FMT_E4M3, FMT_E4M3, MODE_MX4, ODT, PATH_FAST, 1, 5>(p, st);
+  else if (mt <= 2 && pairs) skinny_launch<FMT_E4M3, FMT_E4M3, MODE_MX4_PAIRS, ODT, PATH_FAST, 2, 5>(p, st);
+  else if (mt <= 2) skinny_launch<FMT_E4M3, FMT_E4M3, MODE_MX4, ODT, PATH_FAST, 2, 5>(p, st);
+  else skinny_launch<FMT_E4M3, FMT_E4M3, MODE_MX4, ODT, PATH_FAST, 4, 5>(p, st);
+}
+
 hipError_t launch_gemm_skinny_fp4(const GemmArgs& p, int mode, int odt, hipStream_t st) {
   if (mode == MODE_NV4) {
     if (odt == DT_F32) skinny_nv<DT_F32>(p, st);
     else skinny_nv<DT_BF16>(p, st);
   } else if (odt == DT_F32) {
-    skinny_mt<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_F32, PATH_FAST>(p, st);
+    skinny_mx4<DT_F32>(p, st);
   } else {
-    skinny_mt<FMT_E4M3, FMT_E4M3, MODE_MX4, DT_BF16, PATH_FAST>(p, st);
+    skinny_mx4<DT_BF16>(p, st);
   }
   return hipGetLastError();
 }

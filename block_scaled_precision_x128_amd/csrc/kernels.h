@@ -15,6 +15,10 @@ enum { MODE_EPILOGUE = 0, MODE_PROMOTE = 1, MODE_MX = 2 };
 // FP4 (E2M1, two codes per byte) operands: MXFP4 (UE8M0 per 32 K) and NVFP4
 // (E4M3 microscale per 16 K, fp32 tensor scales ta, tb).
 enum { MODE_MX4 = 3, MODE_NV4 = 4 };
+// Kernel-internal form of MODE_MX4 for K % 512 == 0: a row's scale bytes of
+// 256-K steps 2p and 2p+1 form one 16-byte aligned block, staged with one
+// 16-byte load.
+enum { MODE_MX4_PAIRS = 5 };
 // Matrix-core path: exact products with fp32 sums (bf16 instructions on the
 // expanded codes), or the FP8 instructions' own accumulation.
 enum { PATH_EXACT = 0, PATH_FAST = 1 };

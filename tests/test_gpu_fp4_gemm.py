@@ -109,12 +109,14 @@ def test_fp4_gemm_k_zero():
 
 @pytest.mark.parametrize("out_dt", [fb.DT_F32, fb.DT_BF16])
 @pytest.mark.parametrize("shape", [(16, 18432, 1024), (48, 784, 2048), (64, 5008, 1536),
-                                   (16, 48, 7168)])
+                                   (16, 48, 7168), (32, 784, 1536), (16, 528, 768), (32, 400, 1280)])
 def test_mxfp4_gemm_decode_shapes(out_dt, shape):
     """MXFP4 with M <= 64 runs the skinny kernel on the FP4 matrix cores:
     workgroups own ceil(N / grid) weight rows (72 at N = 18432, not a whole
-    number of 16-row tiles; 20 at N = 5008), the waves split K, and X rows
-    past M read zeros.  Every output is checked."""
+    number of 16-row tiles; 20 at N = 5008), the waves split K (ranges that
+    start on odd steps included), and X rows past M read zeros.  M <= 32 with
+    K % 512 == 0 stages the scale bytes of step pairs, the other shapes word
+    by word.  Every output is checked."""
     M, N, K = shape
     label = f"mxfp4 decode gemm out={out_dt} shape={shape}"
     say(label)
