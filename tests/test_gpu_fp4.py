@@ -150,3 +150,20 @@ def test_fp4_mx_every_bf16_value(dt):
     flat[:vals.size] = vals
     x[:, 1:] = flat.reshape(nblk, per_block)
     _check_quantize(fb.FP4_MX, dt, x.reshape(nblk // 4, 128), f"fp4 MX every bf16 value dt={dt}")
+
+
+@pytest.mark.parametrize("pos", ["last", "fourth_slot"])
+def test_fp4_nv_quantize_many_trips(pos):
+    """NVFP4 at 4096 x 4608 bf16 (18.9 M elements): both passes cap their
+    grids, so every thread loops over several chunks a grid stride apart.
+    The tensor's largest magnitude sits in its last element or in a chunk
+    reached only on a later trip, so a skipped chunk changes the tensor scale
+    and every code."""
+    rng = np.random.default_rng(880 + len(pos))
+    rows, cols = 4096, 4608
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    flat = x.reshape(-1)
+    stride = 2048 * 256                      # chunks of 8 elements per grid stride
+    at = flat.size - 1 if pos == "last" else 8 * (3 * stride + 5) + 3
+    flat[at] = -4096.0
+    _check_quantize(fb.FP4_NV, fb.DT_BF16, x, f"fp4 NV many trips pos={pos}")
