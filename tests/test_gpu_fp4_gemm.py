@@ -47,7 +47,8 @@ def _run(kind, ops, out_dt):
 
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("out_dt", [fb.DT_F32, fb.DT_BF16])
-@pytest.mark.parametrize("shape", [(16, 16, 256), (48, 80, 512), (272, 528, 768), (512, 1024, 2048)])
+@pytest.mark.parametrize("shape", [(16, 16, 256), (48, 80, 512), (272, 528, 768), (512, 1024, 2048),
+                                   (400, 784, 1536)])
 def test_fp4_gemm_small(kind, out_dt, shape):
     M, N, K = shape
     label = f"fp4 gemm kind={kind} out={out_dt} shape={shape}"
