@@ -659,13 +659,15 @@ static void tiled_shape(const GemmArgs& p, hipStream_t st) {
   // right after: e.g. 4096x7168 runs as 256 + 256 tiles in 1.75 tile-times
   // instead of 448 tiles in 2.
   // (The quantized outputs need 64-column wave tiles: no split for them.)
-  // Only the exact path splits.  Its steps are bound by the VALU and matrix
-  // work, which shrinks with the tile.  The FP8 native and MXFP4 paths are
-  // bound per step by load and LDS latency, so a 256x192 tile takes as long
-  // as a 256x256 one.  Measured at 4096x7168x7168 on rotated inputs, one
-  // launch of all 448 tiles was 7-8% faster than the split for FP8 native
-  // and equal for MXFP4.
-  if (PATH == PATH_EXACT && ODT < ODT_Q_E4M3 && big_tiles % cus != 0 && cus % ntm == 0) {
+  // The exact path splits: its steps are bound by the VALU and matrix work,
+  // which shrinks with the tile.  The FP8 native path is bound per step by
+  // load and LDS latency, so a 256x192 tile takes about as long as a 256x256
+  // one; measured at 4096x7168x7168 on rotated inputs, one launch of all 448
+  // tiles was 7-8% faster than the split there.  MXFP4 with step-pair scale
+  // staging splits too: 2% faster, A/B on one box (MXFP4 with word-by-word
+  // staging measured equal either way).
+  if ((PATH == PATH_EXACT || MODE == MODE_MX4_PAIRS) && ODT < ODT_Q_E4M3 && big_tiles % cus != 0 &&
+      cus % ntm == 0) {
     const int64_t wave_cols = (cus / ntm) * 256;
     const int64_t n1 = (p.N / wave_cols) * wave_cols, n2 = p.N - n1;
     if (n1 > 0 && n2 > 0 && ntm * ((n2 + 191) / 192) <= cus) {
