@@ -387,8 +387,8 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       auto frag = [&](const uint8_t* base, int row, int R, int h, Op* x) {
         const u32x4 d = lds16(base, row * 128 + (h ? c1 : c0));
         const uint32_t mw = (&s_e[buf][0][0])[4 * R + g];
-        const v2f m = h ? decode2<FMT_E4M3>(mw, true) : decode2<FMT_E4M3>(mw, false);
-        const v2h m0 = {(_Float16)m.x, (_Float16)m.x}, m1 = {(_Float16)m.y, (_Float16)m.y};
+        v2h m0, m1;
+        e4m3_pair_f16(mw, h, m0, m1);
         x[0] = cvt8_fp4_f16(d.x, m0);
         x[1] = cvt8_fp4_f16(d.y, m0);
         x[2] = cvt8_fp4_f16(d.z, m1);

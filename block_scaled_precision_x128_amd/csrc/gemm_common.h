@@ -120,6 +120,16 @@ __device__ __forceinline__ v8h cvt8_fp4_f16(uint32_t w, v2h m) {
   return v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// The E4M3 microscales in bytes 2h and 2h+1 of w as fp16 pairs {m, m}: the
+// hardware convert with a unit scale, exact (every E4M3 value, NaN included,
+// is an fp16 value).
+__device__ __forceinline__ void e4m3_pair_f16(uint32_t w, int h, v2h& m0, v2h& m1) {
+  const v2h m = h ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+                  : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  m0 = v2h{m[0], m[0]};
+  m1 = v2h{m[1], m[1]};
+}
+
 // The 8 codes of dwords (d0, d1) -> one K=32 bf16 operand.
 template <int FMT>
 __device__ __forceinline__ v8bf cvt8(uint32_t d0, uint32_t d1, float scale) {

@@ -241,8 +241,8 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
       const uint32_t* sw32 = reinterpret_cast<const uint32_t*>(sc);
       auto frag = [&](int off, uint32_t mw, int h, v8h* x) {
         const u32x4 d = lds16(st, off + (h ? c1 : c0));
-        const v2f m = h ? decode2<FMT_E4M3>(mw, true) : decode2<FMT_E4M3>(mw, false);
-        const v2h m0 = {(_Float16)m.x, (_Float16)m.x}, m1 = {(_Float16)m.y, (_Float16)m.y};
+        v2h m0, m1;
+        e4m3_pair_f16(mw, h, m0, m1);
         x[0] = cvt8_fp4_f16(d.x, m0);
         x[1] = cvt8_fp4_f16(d.y, m0);
         x[2] = cvt8_fp4_f16(d.z, m1);
