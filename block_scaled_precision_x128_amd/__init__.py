@@ -79,6 +79,19 @@ _SIGS = {
 }
 EXPORTS = tuple(_SIGS)
 
+# Measurement probes (include/fp8blk_probe.h): not part of the method; they
+# measure the machine's matrix-core, read and copy ceilings.
+PROBE_MFMA_BF16, PROBE_MFMA_FP8 = 0, 1
+_PROBE_SIGS = {
+    "fp8blk_probe_mfma_sink_floats": (_c.c_size_t, [_c.c_int]),
+    "fp8blk_probe_mfma": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.POINTER(_c.c_double),
+                                     _c.c_void_p]),
+    "fp8blk_probe_read_sink_floats": (_c.c_size_t, []),
+    "fp8blk_probe_read": (_c.c_int, [_c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_void_p]),
+    "fp8blk_probe_copy": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p]),
+}
+PROBE_EXPORTS = tuple(_PROBE_SIGS)
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -100,7 +113,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         raise RuntimeError(f"libfp8blk.so not found at {p}: build it with "
                            "`python -m block_scaled_precision_x128_amd.build` (there is no fallback)")
     lib = ctypes.CDLL(p)
-    for name, (res, args) in _SIGS.items():
+    for name, (res, args) in list(_SIGS.items()) + list(_PROBE_SIGS.items()):
         f = getattr(lib, name)
         f.restype = res
         f.argtypes = args
@@ -241,9 +254,16 @@ def fp8_gemm_blockscaled(a, a_fmt: int, a_gran: int, a_scales, b, b_fmt: int, b_
     N = b.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=_torch_dtype(out_dtype), device=a.device)
-    st = load_library().fp8_gemm_blockscaled_ex(
-        a.data_ptr(), a_fmt, a_gran, a_scales.data_ptr(), b.data_ptr(), b_fmt, b_gran, b_scales.data_ptr(),
-        M, N, K, out.data_ptr(), out_dtype, algo, accum, _stream(stream))
+    lib = load_library()
+    if algo == GEMM_AUTO and accum == ACCUM_FP32:
+        # the plain entry point (AUTO kernel choice, exact products with fp32 sums)
+        st = lib.fp8_gemm_blockscaled(
+            a.data_ptr(), a_fmt, a_gran, a_scales.data_ptr(), b.data_ptr(), b_fmt, b_gran, b_scales.data_ptr(),
+            M, N, K, out.data_ptr(), out_dtype, _stream(stream))
+    else:
+        st = lib.fp8_gemm_blockscaled_ex(
+            a.data_ptr(), a_fmt, a_gran, a_scales.data_ptr(), b.data_ptr(), b_fmt, b_gran, b_scales.data_ptr(),
+            M, N, K, out.data_ptr(), out_dtype, algo, accum, _stream(stream))
     _check("fp8_gemm_blockscaled", st)
     return out
 
@@ -361,3 +381,39 @@ def fp4_gemm_blockscaled(a, a_scales, a_tensor_scale, b, b_scales, b_tensor_scal
                                              out.data_ptr(), _dt_of(out), _stream(stream))
     _check("fp4_gemm_blockscaled", st)
     return out
+
+
+# ---- measurement probes (include/fp8blk_probe.h) -------------------------------
+
+def probe_mfma(kind: int, waves_per_simd: int, iters: int, sink=None, stream=None) -> float:
+    """Enqueue the back-to-back MFMA probe; returns the launch's FLOP count."""
+    torch = _torch()
+    lib = load_library()
+    if sink is None:
+        sink = torch.empty(int(lib.fp8blk_probe_mfma_sink_floats(waves_per_simd)), dtype=torch.float32,
+                           device="cuda")
+    flops = ctypes.c_double(0.0)
+    st = lib.fp8blk_probe_mfma(kind, waves_per_simd, iters, sink.data_ptr(), ctypes.byref(flops), _stream(stream))
+    _check("fp8blk_probe_mfma", st)
+    return flops.value
+
+
+def probe_read(src, sink=None, stream=None):
+    """Enqueue a streaming read of every byte of the device tensor src."""
+    torch = _torch()
+    lib = load_library()
+    if sink is None:
+        sink = torch.empty(int(lib.fp8blk_probe_read_sink_floats()), dtype=torch.float32, device=src.device)
+    st = lib.fp8blk_probe_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), _stream(stream))
+    _check("fp8blk_probe_read", st)
+    return sink
+
+
+def probe_copy(src, dst, stream=None):
+    """Enqueue a device copy of src into dst (same byte size, no overlap)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same byte size")
+    st = load_library().fp8blk_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(stream))
+    _check("fp8blk_probe_copy", st)
+    return dst

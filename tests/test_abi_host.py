@@ -12,6 +12,7 @@ import block_scaled_precision_x128_amd as fb
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp8blk.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "fp8blk_probe.h")
 
 
 def _ensure_built():
@@ -20,10 +21,10 @@ def _ensure_built():
         build.build()
 
 
-def header_functions():
-    src = open(HEADER).read()
+def header_functions(path=HEADER, prefix=r"fp[48]_"):
+    src = open(path).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**(fp[48]_\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\**\s+\**(" + prefix + r"\w+)\s*\(", src, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -40,6 +41,33 @@ def test_library_exports_every_declared_symbol(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
     assert lib.fp8_abi_version() == 1
+
+
+def test_probe_header_declares_the_binding_exports(lib):
+    names = header_functions(PROBE_HEADER, r"fp8blk_probe_")
+    assert names == sorted(fb.PROBE_EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_every_header_is_covered():
+    # every header under include/ is one of the two checked above
+    assert sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")) == \
+        ["fp8blk.h", "fp8blk_probe.h"]
+
+
+def test_probe_argument_checks(lib):
+    flops = ctypes.c_double(0.0)
+    assert lib.fp8blk_probe_mfma(7, 2, 1, FAKE, ctypes.byref(flops), None) == 2      # FP8_ERR_ENUM
+    assert lib.fp8blk_probe_mfma(0, 3, 1, FAKE, ctypes.byref(flops), None) == 3      # FP8_ERR_SHAPE
+    assert lib.fp8blk_probe_mfma(0, 2, 0, FAKE, ctypes.byref(flops), None) == 3
+    assert lib.fp8blk_probe_mfma(0, 2, 1, None, ctypes.byref(flops), None) == 1      # FP8_ERR_NULL
+    assert lib.fp8blk_probe_read(FAKE, 15, FAKE, None) == 3
+    assert lib.fp8blk_probe_read(FAKE + 4, 16, FAKE, None) == 7                       # FP8_ERR_ALIGN
+    assert lib.fp8blk_probe_copy(FAKE, FAKE + 64, 1024, None) == 3                     # overlapping
+    assert lib.fp8blk_probe_copy(None, FAKE, 16, None) == 1
+    assert lib.fp8blk_probe_read_sink_floats() == 2048 * 256
+    assert lib.fp8blk_probe_mfma_sink_floats(3) == 0
 
 
 def test_status_strings(lib):
@@ -217,7 +245,7 @@ def test_fp4_validation(lib):
 
 
 def test_library_exports_nothing_else(lib):
-    """The C symbols the library exports are exactly the header's functions."""
+    """The C symbols the library exports are exactly the headers' functions."""
     import shutil
     import subprocess
     nm = shutil.which("nm")
@@ -225,7 +253,7 @@ def test_library_exports_nothing_else(lib):
         pytest.skip("nm not available")
     out = subprocess.run([nm, "-D", "--defined-only", fb.LIB_PATH], capture_output=True, text=True, check=True).stdout
     c_syms = sorted(l.split()[-1] for l in out.splitlines() if " T " in l and not l.split()[-1].startswith("_Z"))
-    assert c_syms == header_functions()
+    assert c_syms == sorted(header_functions() + header_functions(PROBE_HEADER, r"fp8blk_probe_"))
 
 
 def test_fp4_gemm_validation(lib):
