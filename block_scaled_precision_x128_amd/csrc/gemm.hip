@@ -122,6 +122,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   constexpr int SC = (SCALE_CHUNKS + NW - 1) / NW;     // scale loads per wave per (even) step
   constexpr int LOADS = LPW + SC;                      // loads per wave per step (MODE_MX4_PAIRS: even steps)
   constexpr int ES = PAIRS ? 2 : NS;                   // scale stages
+  constexpr bool MX_WORDS = MODE == MODE_MX && PATH == PATH_EXACT;   // exact MX: scale words read per step
   static_assert((NS - 1) * LOADS <= 63, "loads in flight must fit the vmcnt counter");
   static_assert(TBM % 64 == 0 && (TBM + TBN) % 64 == 0, "scale loads move 64 rows at a time");
   // NS LDS stages; the loads of the next NS-1 K steps are in flight while one is computed.
@@ -267,10 +268,11 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   for (int j = 0; j < NS - 1; ++j)
     if (j < nkb) issue_loads(j, j);
 
-  int buf = 0;   // stage of step kb
-  for (int kb = 0; kb < nkb; ++kb) {
-    // Wait for this step's loads; those of later steps stay in flight (every
-    // wave issues LOADS per step, and loads complete in issue order).
+  // Wait for step kb's loads (those of later steps stay in flight: every wave
+  // issues LOADS per step, and loads complete in issue order), publish the
+  // stage to every wave, then reuse the stage read in the previous step for
+  // step kb + NS - 1.
+  auto sync_step = [&](int kb, int buf) {
     if constexpr (NS == 3) {
       // (MODE_MX4_PAIRS: odd steps issue no scale loads)
       if (kb + 1 < nkb) {
@@ -284,8 +286,29 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
-    // The stage read in the previous step is free now: load step kb+NS-1 into it.
     if (kb + NS - 1 < nkb) issue_loads(kb + NS - 1, buf == 0 ? NS - 1 : buf - 1);
+  };
+
+  int buf = 0;   // stage of step kb
+  int kb = 0;
+  bool mx_wide = false;   // exact MX: a step whose exponents cannot be folded (below)
+  for (; kb < nkb; ++kb) {
+    sync_step(kb, buf);
+    if constexpr (MX_WORDS) {
+      // Folding 2^e into an operand's bf16 expansion is exact and finite only
+      // for e in a range (mx_fold_exact); the first step with an exponent
+      // outside it (for any row of the wave) hands this and every later step
+      // to the block-by-block loop below.
+      bool w = false;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) w |= !mx_fold_exact<AF>((s_e[buf][0][a_row0 + 16 * i] >> (8 * g)) & 0xffu);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) w |= !mx_fold_exact<BF>((s_e[buf][0][TBM + b_row0 + 16 * j] >> (8 * g)) & 0xffu);
+      if (__builtin_amdgcn_ballot_w64(w) != 0) {
+        mx_wide = true;
+        break;
+      }
+    }
 
     const uint8_t* sa_ = &smem[buf][0];
     const uint8_t* sb_ = &smem[buf][TBM * TBK];
@@ -495,6 +518,48 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       }
     }
     buf = buf + 1 == NS ? 0 : buf + 1;
+  }
+
+  if constexpr (MX_WORDS) {
+    // Block-by-block exact MX: one 32-K block b of the step per instruction,
+    // lane group g taking K 32b + 8g .. +7 of its row, the codes expanded with
+    // a unit scale (exact), so an instruction's sum P is one block's exact
+    // products summed in fp32; P * 2^(eA + eB) joins the accumulator through an
+    // exact ldexp (eA of the output row, eB of the output column).  Steps kb ..
+    // nkb-1 (the first one's loads are already waited for and published).
+    for (bool first = true; mx_wide && kb < nkb; ++kb, first = false) {
+      if (!first) sync_step(kb, buf);
+      const uint8_t* sa_ = &smem[buf][0];
+      const uint8_t* sb_ = &smem[buf][TBM * TBK];
+#pragma unroll 1
+      for (int b = 0; b < 4; ++b) {
+        const int cb = (((2 * b + (g >> 1)) ^ sw_) << 4) + 8 * (g & 1);
+        v8bf xbb[NJ];
+        int ebj[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const uint2 d = *reinterpret_cast<const uint2*>(sb_ + (b_row0 + 16 * j) * 128 + cb);
+          xbb[j] = cvt8<BF>(d.x, d.y, 1.0f);
+          ebj[j] = (int)((s_e[buf][0][TBM + b_row0 + 16 * j] >> (8 * b)) & 0xffu) - 127;
+        }
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const uint2 d = *reinterpret_cast<const uint2*>(sa_ + (a_row0 + 16 * i) * 128 + cb);
+          const v8bf xa = cvt8<AF>(d.x, d.y, 1.0f);
+          // UE8M0 words of the tile's output rows 4g .. 4g+3
+          const u32x4 wq = *reinterpret_cast<const u32x4*>(&s_e[buf][0][wm * WR + 16 * i + 4 * g]);
+          const int ea[4] = {(int)((wq.x >> (8 * b)) & 0xffu) - 127, (int)((wq.y >> (8 * b)) & 0xffu) - 127,
+                             (int)((wq.z >> (8 * b)) & 0xffu) - 127, (int)((wq.w >> (8 * b)) & 0xffu) - 127};
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const v4f pb = mfma_bf16(xa, xbb[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[i][j][q] += __builtin_amdgcn_ldexpf(pb[q], ea[q] + ebj[j]);
+          }
+        }
+      }
+      buf = buf + 1 == NS ? 0 : buf + 1;
+    }
   }
 
   // epilogue

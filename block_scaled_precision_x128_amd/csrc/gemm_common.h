@@ -138,6 +138,18 @@ __device__ __forceinline__ v8bf cvt8(uint32_t d0, uint32_t d1, float scale) {
   return v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+// Whether folding the MX block scale 2^(byte - 127) into the bf16 expansion
+// of FMT codes is exact and stays in bf16's normal range: every nonzero code
+// times 2^e lies in [2^-126, 2^128) when e is in [-117, 119] (E4M3: codes
+// 2^-9 .. 448) or [-110, 112] (E5M2: codes 2^-16 .. 57344).  Outside that
+// range the GEMMs apply 2^(eA + eB) to each 32-K block's fp32 sum instead.
+template <int FMT>
+__device__ __forceinline__ bool mx_fold_exact(uint32_t byte) {
+  constexpr uint32_t lo = FMT == FMT_E4M3 ? 127 - 117 : 127 - 110;
+  constexpr uint32_t hi = FMT == FMT_E4M3 ? 127 + 119 : 127 + 112;
+  return byte - lo <= hi - lo;
+}
+
 // 2^(byte - 127) as fp32 (byte 0 gives the subnormal 2^-127).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t byte) {
   return byte ? __uint_as_float(byte << 23) : __uint_as_float(0x00400000u);

@@ -290,6 +290,53 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
         }
       }
     } else {
+      // MX steps whose UE8M0 exponents leave the range in which folding 2^e
+      // into an operand's bf16 conversion is exact and finite go block by
+      // block: one 32-K block per instruction on unit-scale expansions (exact),
+      // each block's fp32 sum added times 2^(eA + eB) with an exact ldexp.
+      bool mx_wide = false;
+      if constexpr (MODE == MODE_MX) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) mx_wide |= !mx_fold_exact<AF>(ea[mt]);
+#pragma unroll
+        for (int t = 0; t < T; ++t) mx_wide |= !mx_fold_exact<BF>(eb[t]);
+        mx_wide = __builtin_amdgcn_ballot_w64(mx_wide) != 0;
+      }
+      if (MODE == MODE_MX && mx_wide) {
+        const uint32_t* sw32 = reinterpret_cast<const uint32_t*>(sc);
+#pragma unroll 1
+        for (int b = 0; b < 4; ++b) {
+          // lane group g: K 32b + 8g .. +7 of its row (logical chunk 2b + g/2)
+          const int cb = (((2 * b + (g >> 1)) ^ swz) << 4) + 8 * (g & 1);
+          v8bf xab[MT];
+          int eam[MT][4];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const uint2 d = *reinterpret_cast<const uint2*>(st + St::kW + 16 * mt * 128 + rlane + cb);
+            xab[mt] = cvt8<AF>(d.x, d.y, 1.0f);
+            // X scale words of the tile's output rows 4g .. 4g+3
+            const u32x4 wq = *reinterpret_cast<const u32x4*>(sw32 + 16 * mt + 4 * g);
+            eam[mt][0] = (int)((wq.x >> (8 * b)) & 0xffu) - 127;
+            eam[mt][1] = (int)((wq.y >> (8 * b)) & 0xffu) - 127;
+            eam[mt][2] = (int)((wq.z >> (8 * b)) & 0xffu) - 127;
+            eam[mt][3] = (int)((wq.w >> (8 * b)) & 0xffu) - 127;
+          }
+#pragma unroll
+          for (int t = 0; t < T; ++t) {
+            const uint2 d = *reinterpret_cast<const uint2*>(st + 16 * t * 128 + rlane + cb);
+            const v8bf xbb = cvt8<BF>(d.x, d.y, 1.0f);
+            // the lane's own W row (its output column)
+            const int ebt = (int)((sw32[64 + 16 * t + (lane & 15)] >> (8 * b)) & 0xffu) - 127;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              const v4f pb = mfma_bf16(xab[mt], xbb, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[mt][t][q] += __builtin_amdgcn_ldexpf(pb[q], eam[mt][q] + ebt);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // one column tile at a time (register pressure)
+          }
+        }
+      } else {
       // X expanded once per step and reused for every column tile.
       v8bf xa[MT][4];
 #pragma unroll
@@ -327,6 +374,7 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
             for (int s4 = 0; s4 < 4; ++s4) acc[mt][t] = mfma_bf16(xa[mt][s4], xb[s4], acc[mt][t]);
           }
         }
+      }
       }
     }
   };

@@ -10,7 +10,8 @@
 
 namespace fp8blk {
 
-constexpr int kProbeBlocks = 2048;   // workgroups of the read and copy probes
+constexpr int kReadBlocks = 1024;    // workgroups of the read probe
+constexpr int kCopyBlocks = 2048;    // workgroups of the copy probe
 constexpr int kChains = 8;           // independent accumulators per wave
 
 // Each wave issues `iters` rounds of kChains independent MFMAs on operands
@@ -49,30 +50,44 @@ __global__ __launch_bounds__(512) void k_probe_mfma(float* sink, int iters) {
   sink[(int64_t)blockIdx.x * blockDim.x + t] = s;
 }
 
+// Each workgroup streams one contiguous chunk, eight 16-byte loads in flight
+// per thread (a grid-stride loop over the whole buffer measured 5.3 TB/s
+// against 6.0 for contiguous chunks).
 __global__ __launch_bounds__(256) void k_probe_read(const u32x4* src, int64_t n16, uint32_t* sink) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  constexpr int U = 8;
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t b0 = (int64_t)blockIdx.x * per, b1 = b0 + per < n16 ? b0 + per : n16;
+  int64_t i = b0 + threadIdx.x;
   uint32_t x = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
-    x ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w ^ v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^ v3.w;
+  for (; i + (U - 1) * 256 < b1; i += U * 256) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < b1; i += 256) {
     const u32x4 v = src[i];
     x ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = x;
 }
 
+// The same chunking, eight loads in flight, non-temporal loads and stores
+// (5.57 TB/s of read + write against 5.3 with ordinary ones).
 __global__ __launch_bounds__(256) void k_probe_copy(const u32x4* src, u32x4* dst, int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + stride < n16; i += 2 * stride) {
-    const u32x4 v0 = src[i], v1 = src[i + stride];
-    dst[i] = v0;
-    dst[i + stride] = v1;
+  constexpr int U = 8;
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t b0 = (int64_t)blockIdx.x * per, b1 = b0 + per < n16 ? b0 + per : n16;
+  int64_t i = b0 + threadIdx.x;
+  for (; i + (U - 1) * 256 < b1; i += U * 256) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(&src[i + u * 256]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(v[u], &dst[i + u * 256]);
   }
-  for (; i < n16; i += stride) dst[i] = src[i];
+  for (; i < b1; i += 256) dst[i] = src[i];
 }
 
 }  // namespace fp8blk
@@ -100,13 +115,13 @@ int fp8blk_probe_mfma(int kind, int waves_per_simd, int iters, float* sink, doub
   return hipGetLastError() == hipSuccess ? FP8_OK : FP8_ERR_HIP;
 }
 
-size_t fp8blk_probe_read_sink_floats(void) { return (size_t)kProbeBlocks * 256u; }
+size_t fp8blk_probe_read_sink_floats(void) { return (size_t)kReadBlocks * 256u; }
 
 int fp8blk_probe_read(const void* src, int64_t bytes, float* sink, hipStream_t stream) {
   if (!src || !sink) return FP8_ERR_NULL;
   if (bytes < 0 || bytes % 16 != 0) return FP8_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(src) % 16 != 0) return FP8_ERR_ALIGN;
-  hipLaunchKernelGGL(k_probe_read, dim3(kProbeBlocks), dim3(256), 0, stream, static_cast<const u32x4*>(src),
+  hipLaunchKernelGGL(k_probe_read, dim3(kReadBlocks), dim3(256), 0, stream, static_cast<const u32x4*>(src),
                      bytes / 16, reinterpret_cast<uint32_t*>(sink));
   return hipGetLastError() == hipSuccess ? FP8_OK : FP8_ERR_HIP;
 }
@@ -117,7 +132,7 @@ int fp8blk_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t str
   if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0) return FP8_ERR_ALIGN;
   const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
   if (s0 < d0 + (uintptr_t)bytes && d0 < s0 + (uintptr_t)bytes && bytes > 0) return FP8_ERR_SHAPE;
-  hipLaunchKernelGGL(k_probe_copy, dim3(kProbeBlocks), dim3(256), 0, stream, static_cast<const u32x4*>(src),
+  hipLaunchKernelGGL(k_probe_copy, dim3(kCopyBlocks), dim3(256), 0, stream, static_cast<const u32x4*>(src),
                      static_cast<u32x4*>(dst), bytes / 16);
   return hipGetLastError() == hipSuccess ? FP8_OK : FP8_ERR_HIP;
 }

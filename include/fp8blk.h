@@ -197,9 +197,21 @@ fp8_status_t fp8_cast(const void* x, fp8_dtype_t x_dt, int64_t n, fp8_format_t f
  *   TILE_1x128 x BLOCK_128x128 each 128-K partial product is scaled by
  *                              sA[m,kb] * sB[n/128,kb] and added to an fp32
  *                              accumulator (promotion every 128 K)
- *   MX32 x MX32                power-of-two scales applied per 32-K block by
- *                              the scaled matrix-core instruction
+ *   MX32 x MX32                power-of-two scales 2^(eA + eB) applied per
+ *                              32-K block: folded exactly into the operands'
+ *                              expansion while every code times 2^e stays in
+ *                              bf16's normal range (e in [-117, 119] for E4M3,
+ *                              [-110, 112] for E5M2), else applied to each
+ *                              block's fp32 sum; the native accumulation gives
+ *                              the bytes to the scaled matrix-core instruction
  * Any other pair returns FP8_ERR_UNSUPPORTED.  Formats may differ per operand.
+ * Accuracy (FP8_ACCUM_FP32): |out - exact| <= 1e-4 * sum_k |x_k w_k| holds for
+ * every code and every UE8M0 exponent, including operands whose decoded values
+ * alone lie outside fp32's range (a code times 2^e up to 2^128 or down to
+ * 2^-136), as long as every scaled product x_k w_k, every partial sum and the
+ * result lie in fp32's normal range [2^-126, 2^128).  A result outside that
+ * range cannot be represented to that accuracy in fp32 (it under- or
+ * overflows); a bf16 output adds its own rounding, half a bf16 ulp.
  * Shapes: M % 16 == 0, N % 16 == 0, K % 128 == 0, K <= 2^22 (the kernels
  * address up to 256 operand rows through 32-bit buffer offsets); N % 128 == 0
  * for a BLOCK_128x128 b.  K == 0 writes zeros. */

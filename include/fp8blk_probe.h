@@ -48,13 +48,14 @@ int fp8blk_probe_mfma(int kind, int waves_per_simd, int iters, float* sink, doub
 size_t fp8blk_probe_read_sink_floats(void);
 
 /* Streaming read of `bytes` bytes at src (16-byte aligned, bytes % 16 == 0):
- * every byte is loaded once with 16-byte loads, four in flight per thread, and
- * folded into one word per thread written to sink (fp8blk_probe_read_sink_floats()
- * floats). */
+ * every byte is loaded once with 16-byte loads, each workgroup streaming one
+ * contiguous chunk with eight loads in flight per thread, and folded into one
+ * word per thread written to sink (fp8blk_probe_read_sink_floats() floats). */
 int fp8blk_probe_read(const void* src, int64_t bytes, float* sink, hipStream_t stream);
 
 /* Device copy of `bytes` bytes from src to dst (both 16-byte aligned, bytes %
- * 16 == 0, not overlapping) with 16-byte loads and stores. */
+ * 16 == 0, not overlapping) with 16-byte non-temporal loads and stores, one
+ * contiguous chunk per workgroup, eight loads in flight per thread. */
 int fp8blk_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
 #ifdef __cplusplus

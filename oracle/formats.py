@@ -12,15 +12,17 @@ Formats, as the pages state them:
     max 57344, min normal 2^-14 ("The FP8 Family", format table; "FP8
     Mixed-Precision Serving", "Core Architectural Differences").  The pages do
     not write E5M2's subnormal rule; the IEEE rule 2^-14 * M/4 is used, by
-    analogy with E4M3's and with "stays IEEE-compliant".
+    analogy with E4M3's and with the page's remark that E5M2 keeps IEEE
+    conventions.
   * Generic value formula x = (-1)^s 2^(e-bias) (1 + sum b_i 2^-i)
     ("FP8 Mixed-Precision Serving", "The Mathematics of FP8").
 
 Cast (fp32 value -> code), "clip(round(x/s), fp8_min, fp8_max)" with s = 1
 ("The FP8 Family", "Scaling is what makes FP8 usable"; "FP8 Mixed-Precision
-Serving", per-tensor scaling formula) and ".rn = round to nearest even;
-.satfinite = clamp on overflow" ("Illustrated GPU kernels, Part 8", qdq listing
-comments):
+Serving", per-tensor scaling formula), rounding to nearest with ties to even
+and clamping finite overflow to the format's largest value (the rounding and
+saturation modifiers the comments of the qdq listing in "Illustrated GPU
+kernels, Part 8" explain):
   * finite |v| > Vmax -> +-Vmax;
   * otherwise the nearest finite code, ties to the even mantissa;
   * the sign is kept, also for zero results (-0 and small negatives -> 0x80);

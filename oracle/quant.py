@@ -24,8 +24,9 @@ What is computed, with where the pages say it:
   * UE8M0 scale: eight exponent bits, no mantissa, a pure power of two ("Part 8",
     OCP MX paragraph).  The pages give no rule for choosing the exponent.  The
     reading taken: the smallest power of two 2^e with amax <= Vmax * 2^e, so the
-    block's largest element "lands near the top of the range" ("Part 8", the
-    paragraph before the qdq listing) and no element saturates.  The byte is
+    block's largest element falls in the format's top binade, as the pages ask
+    of a well-chosen scale ("Part 8", the paragraph before the qdq listing), and
+    no element saturates.  The byte is
     e + 127 with e clamped to [-127, 127]; byte 255 is never produced and
     decodes to NaN.
   * amax = 0 (or amax / Vmax rounding to 0 in fp32): s = 1.0, MX e = -127; all

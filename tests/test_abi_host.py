@@ -66,7 +66,7 @@ def test_probe_argument_checks(lib):
     assert lib.fp8blk_probe_read(FAKE + 4, 16, FAKE, None) == 7                       # FP8_ERR_ALIGN
     assert lib.fp8blk_probe_copy(FAKE, FAKE + 64, 1024, None) == 3                     # overlapping
     assert lib.fp8blk_probe_copy(None, FAKE, 16, None) == 1
-    assert lib.fp8blk_probe_read_sink_floats() == 2048 * 256
+    assert lib.fp8blk_probe_read_sink_floats() == 1024 * 256
     assert lib.fp8blk_probe_mfma_sink_floats(3) == 0
 
 

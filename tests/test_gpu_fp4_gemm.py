@@ -175,3 +175,41 @@ def test_mxfp4_gemm_block_sums_exact(M):
     out = _run(fb.FP4_MX, (a, sa, None, b, sb, None), fb.DT_F32)
     ref, absb = fp4.gemm_ref(fb.FP4_MX, a, sa, b, sb)
     gemm_check(out, fb.DT_F32, ref, absb, label, rel=1e-5)
+
+
+def _crafted_nv(rows, K, rng):
+    """NVFP4 operands: E2M1 codes with one +-6 among +-0.5s per 16-element
+    block (a -+6 cancelling it in some blocks), and E4M3 microscales drawn over
+    E4M3's whole finite range (subnormal 2^-9 .. 448), so that one matrix-core
+    instruction, which takes 8 elements from each of four blocks, holds
+    products from 0.5 * 2^-9 * 0.5 * 2^-9 up to 2688 * 2688."""
+    codes = np.where(rng.random((rows, K)) < 0.5, 0x1, 0x9).astype(np.uint8)
+    blk = codes.reshape(rows, K // 16, 16)
+    blk[:, :, 0] = np.where(rng.random((rows, K // 16)) < 0.5, 0x7, 0xF)
+    cancel = rng.random((rows, K // 16)) < 0.3
+    blk[:, :, 1] = np.where(cancel, blk[:, :, 0] ^ 0x8, blk[:, :, 1])
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    micro = rng.integers(0x01, 0x7F, (rows, K // 16)).astype(np.uint8)      # 0x7F (NaN) excluded
+    micro[:, ::7] = 0x7E                                                     # 448, the top
+    return packed, micro
+
+
+@pytest.mark.parametrize("M", [16, 128])
+def test_nvfp4_gemm_fp16_matrix_core_sums(M):
+    """NVFP4 runs on the fp16 matrix cores with each code times its E4M3
+    microscale expanded exactly to fp16.  Crafted operands put a product of
+    2688 * 2688 next to products of 2^-20 inside one instruction, with
+    cancelling pairs: the result must stay within 1e-5 sum_k |x w| (ten times
+    inside the contract), which a truncating in-instruction sum like the FP8
+    instructions' would break.  M = 16 runs the skinny kernel, M = 128 the
+    tiled one."""
+    rng = np.random.default_rng(5151 + M)
+    N, K = 256, 2048
+    a, sa = _crafted_nv(M, K, rng)
+    b, sb = _crafted_nv(N, K, rng)
+    one = np.ones(1, np.float32)
+    label = f"nvfp4 crafted blocks M={M}"
+    say(label)
+    out = _run(fb.FP4_NV, (a, sa, one, b, sb, one), fb.DT_F32)
+    ref, absb = fp4.gemm_ref(fb.FP4_NV, a, sa, b, sb, one[0], one[0])
+    gemm_check(out, fb.DT_F32, ref, absb, label, rel=1e-5)

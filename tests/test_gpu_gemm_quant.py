@@ -49,11 +49,16 @@ def test_fused_quant_matches_quantized_fp32_result(xg, wg, out_fmt):
                                                           accum=accum)
             torch.cuda.synchronize()
             yh = host(yf)
+            # 1x128 tiles are per row: large results are checked on a sample of rows
+            rows = np.arange(M) if M <= 512 else np.random.default_rng(M).choice(M, 96, replace=False)
             if M * N <= 1 << 18:
                 ref, absb = gemm.gemm_ref(xq, sx, xg, fb.E4M3, wq, sw, wg, fb.E4M3)
                 gemm_check(yh, fb.DT_F32, ref, absb, label + " fp32 result", rel)
-            # 1x128 tiles are per row: large results are checked on a sample of rows
-            rows = np.arange(M) if M <= 512 else np.random.default_rng(M).choice(M, 96, replace=False)
+            else:
+                # the sampled rows of the fp32 result against the oracle (row scales follow the rows)
+                sxr = sx if xg == T else sx[rows]
+                ref, absb = gemm.gemm_ref(xq[rows], sxr, xg, fb.E4M3, wq, sw, wg, fb.E4M3)
+                gemm_check(yh[rows], fb.DT_F32, ref, absb, label + " fp32 result (sampled rows)", rel)
             want_q, want_s = oracle_quantize(yh[rows], TL, out_fmt)
             assert_scales_equal(host(scales)[rows], want_s, label)
             assert_codes_equal(host(codes)[rows], want_q, label + " codes", yh[rows])

@@ -148,6 +148,80 @@ def test_nv_tiny_block_and_zero_tensor():
     assert s_t == 1.0 and not fp4.unpack(q).any() and not m.any()
 
 
+def _e2m1_bits_value(code: int) -> Fraction:
+    """E2M1 nibble -> exact value from its bit fields (bias 1, subnormal 0.5)."""
+    e, m = (code >> 1) & 3, code & 1
+    mag = Fraction(m, 2) if e == 0 else Fraction(2) ** (e - 1) * (1 + Fraction(m, 2))
+    return -mag if code & 8 else mag
+
+
+def _e4m3_bits_value(code: int):
+    """E4M3 byte -> exact value from its bit fields, or None for NaN (S.1111.111)."""
+    e, m = (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return None
+    mag = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else Fraction(2) ** (e - 7) * (1 + Fraction(m, 8))
+    return -mag if code & 0x80 else mag
+
+
+def test_dequantize_nv_against_fractions():
+    """dequantize_nv element by element against an independent decode: every
+    E2M1 code under every E4M3 microscale code (NaN, +-0 and subnormal
+    microscales included) and four tensor scales, with S = RN32(m * s_t) and
+    y = RN32(q * S) rounded from exact rationals; NaN where the microscale is
+    NaN, and the sign of a zero result is the sign of q * S."""
+    codes = np.arange(16, dtype=np.uint8)
+    for s_t in (np.float32(1.0), np.float32(3.0517578e-05), np.float32(0.0123456789), np.float32(7.25e+30)):
+        micro = np.arange(256, dtype=np.uint8).reshape(16, 16)          # 16 rows x 16 blocks: every code
+        rows, nblk = micro.shape
+        q = np.tile(codes, (rows, nblk))                                # each block holds the 16 codes
+        y = fp4.dequantize_nv(fp4.pack(q), micro, s_t)
+        assert y.dtype == np.float32 and y.shape == (rows, 16 * nblk)
+        for r in range(rows):
+            for b in range(nblk):
+                mv = _e4m3_bits_value(int(micro[r, b]))
+                for k in range(16):
+                    got = y[r, 16 * b + k]
+                    if mv is None:
+                        assert np.isnan(got)
+                        continue
+                    S = rn32_exact(mv * Fraction(float(s_t)))
+                    qv = _e2m1_bits_value(int(q[r, 16 * b + k]))
+                    want = rn32_exact(qv * Fraction(float(S)))
+                    if want == 0:
+                        # zero microscale codes carry their sign into S (s_t > 0 here)
+                        s_neg = bool(micro[r, b] & 0x80) if mv == 0 else bool(S < 0)
+                        neg = (int(q[r, 16 * b + k]) >= 8) != s_neg
+                        assert got == 0 and bool(np.signbit(got)) == neg, (r, b, k)
+                    else:
+                        assert got.view(np.uint32) == want.view(np.uint32), (r, b, k, got, want)
+
+
+def test_nv_exact_multiples_round_trip():
+    """x built as exact multiples q * m * s_t (s_t a power of two, every block
+    holding a +-6 code, the largest microscale 448) quantizes back to the same
+    codes, microscales and tensor scale, and dequantizes to x bit for bit."""
+    rng = np.random.default_rng(11)
+    rows, nblk = 8, 12
+    s_t = np.float32(2.0 ** -9)
+    mags = [0.5, 1, 1.5, 2, 3, 4, 6]
+    micro_vals = [Fraction(v) for v in (448, 0.25, 1.125, 3.5, 40, 96, 240, 0.015625)]
+    x = np.zeros((rows, 16 * nblk), np.float32)
+    want_m = np.zeros((rows, nblk), np.uint8)
+    for r in range(rows):
+        for b in range(nblk):
+            mv = micro_vals[(r * nblk + b) % len(micro_vals)] if (r, b) != (0, 0) else Fraction(448)
+            want_m[r, b] = formats.encode(np.float64(float(mv)), E4M3)
+            q = rng.choice(mags, 16) * rng.choice([-1.0, 1.0], 16)
+            q[rng.integers(16)] = 6.0 * rng.choice([-1.0, 1.0])
+            for k in range(16):
+                x[r, 16 * b + k] = np.float32(float(Fraction(q[k]) * mv * Fraction(float(s_t))))
+    packed, m, st = fp4.quantize_nv(x)
+    assert st == s_t and np.array_equal(m, want_m)
+    y = fp4.dequantize_nv(packed, m, st)
+    assert np.array_equal(y.view(np.uint32), x.view(np.uint32))
+
+
 @pytest.mark.parametrize("kind", [fp4.MX, fp4.NV])
 def test_gemm_ref_matches_fractions(kind):
     rng = np.random.default_rng(11 + kind)

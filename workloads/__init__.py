@@ -6,9 +6,9 @@ the bf16 storage cast of the inputs.  None of the FP8 method's arithmetic
 (amax, scales, FP8 rounding, GEMM) lives here.
 
 The five workloads mirror the shapes and statistics the pages describe:
-activations ~N(0,1) with a few outlier channels "one or two orders of magnitude
-larger" than the rest (page "Illustrated GPU kernels, Part 8", the outlier
-paragraph after the qdq listing), weights "tightly clustered around zero"
+activations ~N(0,1) with a few outlier channels ten to a hundred times larger
+than the rest (page "Illustrated GPU kernels, Part 8", the outlier paragraph
+after the qdq listing), weights concentrated near zero with a small spread
 (page "FP8 Serving", results section 1), and gradient-like data spanning many
 orders of magnitude for the E5M2 operand (page "The FP8 Family", E5M2 row of
 the format table).
