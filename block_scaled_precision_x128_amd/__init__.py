@@ -45,6 +45,8 @@ _SIGS = {
     "fp8_quantize_workspace_bytes": (_c.c_size_t, [_c.c_int64, _c.c_int64, _c.c_int]),
     "fp8_quantize": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int, _c.c_int,
                                 _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "fp8_quantize_noalloc": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int, _c.c_int,
+                                        _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "fp8_quantize_delayed": (_c.c_int, [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p,
                                         _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_void_p,
                                         _c.c_void_p, _c.c_size_t, _c.c_void_p]),
@@ -197,6 +199,17 @@ def fp8_quantize(x, fmt: int, gran: int, q=None, scales=None, workspace=None, st
     st = lib.fp8_quantize(x.data_ptr(), _dt_of(x), rows, cols, fmt, gran, q.data_ptr(), scales.data_ptr(),
                           _ptr(workspace), wsb, _stream(stream))
     _check("fp8_quantize", st)
+    return q, scales
+
+
+def fp8_quantize_noalloc(x, fmt: int, gran: int, q, scales, stream=None):
+    """fp8_quantize into caller-provided q and scales with no workspace: the
+    per-tensor amax partials live in the library's static device scratch
+    (calls that overlap on one GPU race).  Returns (q, scales)."""
+    rows, cols = x.shape
+    st = load_library().fp8_quantize_noalloc(x.data_ptr(), _dt_of(x), rows, cols, fmt, gran, q.data_ptr(),
+                                             scales.data_ptr(), _stream(stream))
+    _check("fp8_quantize_noalloc", st)
     return q, scales
 
 

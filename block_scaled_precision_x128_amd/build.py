@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8blk.so")
 ARCH = "gfx950"
 
-SOURCES = ["quantize.hip", "dequantize.hip", "gemm.hip", "gemm_skinny.hip", "kv_cache.hip", "fp4.hip", "probes.hip", "abi.cpp"]
+SOURCES = ["quantize.hip", "dequantize.hip", "gemm.hip", "gemm_skinny.hip", "kv_cache.hip", "fp4.hip", "probes.hip", "noalloc.hip", "abi.cpp"]
 # -packed-fp32-ops: keep hipcc from forming packed fp32 arithmetic
 # (v_pk_fma_f32 and friends) out of ordinary float code.
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",

@@ -146,6 +146,22 @@ fp8_status_t fp8_quantize(const void* x, fp8_dtype_t x_dt, int64_t rows, int64_t
                           uint8_t* q, void* scales, void* workspace, size_t ws_bytes,
                           hipStream_t stream);
 
+/* fp8_quantize for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results as fp8_quantize without the workspace: the one
+ * granularity that needs scratch (FP8_GRAN_TENSOR: per-workgroup amax partials)
+ * uses a static 32 KiB device array of the library instead, which covers every
+ * tensor size (FP8_ERR_WORKSPACE would report a need beyond it).  Each GPU holds
+ * its own copy of that array until the process ends; its device address is
+ * looked up on the first call on a device (that call alone makes HIP runtime
+ * queries besides the launches; none allocates).  Every call on a GPU shares
+ * the array, so per-tensor calls that overlap on one GPU (concurrent streams or
+ * threads) race and give undefined results; calls ordered on one stream are
+ * safe.  Nothing in the array needs clearing between calls. */
+fp8_status_t fp8_quantize_noalloc(const void* x, fp8_dtype_t x_dt, int64_t rows, int64_t cols,
+                                  fp8_format_t fmt, fp8_granularity_t g, uint8_t* q, void* scales,
+                                  hipStream_t stream);
+
 /* Quantize a whole [rows, cols] tensor with delayed scaling ("FP8
  * Mixed-Precision Serving", section "Quantization Granularity and Scaling
  * Topologies", delayed scaling): the scale comes from a history of the amax
