@@ -152,10 +152,12 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
   };
 
   // Fragment reads: row r = 16 t + (lane & 15) of the stage, chunks (2g, 2g+1)
-  // on the exact path (K 32g..32g+31), (g, 4+g) on the fast path.
+  // (K 32g..32g+31), except for the scaled instruction on MX and MXFP4
+  // operands, whose lane group g must hold 32-K block g: chunks (g, 4+g).
   const int swz = lds_swz(lane & 15);
-  const int c0 = ((PATH == PATH_EXACT ? 2 * g : g) ^ swz) << 4;
-  const int c1 = ((PATH == PATH_EXACT ? 2 * g + 1 : 4 + g) ^ swz) << 4;
+  constexpr bool kPairedChunks = PATH == PATH_EXACT || (MODE != MODE_MX && !FP4);
+  const int c0 = ((kPairedChunks ? 2 * g : g) ^ swz) << 4;
+  const int c1 = ((kPairedChunks ? 2 * g + 1 : 4 + g) ^ swz) << 4;
   const int rlane = (lane & 15) * 128;
   bool hi[T];
 #pragma unroll
