@@ -285,13 +285,14 @@ class Timer:
     that keeps the GPU busy while the host queues the launches, so the timed
     launches run back to back with no host gaps; between the spin and the
     timed launches sits an untimed pre-roll of the same work lasting at least
-    `preroll_ms`, so the timed launches start at the engine clock a sustained
-    load runs at (right after an idle spin the clock is low for the first
-    milliseconds).  HIP events on the launch stream bracket exactly `reps`
+    `preroll_ms` (at most 3000 iterations), so the timed launches start at the
+    engine clock a sustained load runs at: after a spin or an idle host the
+    c3 GEMM starts about 20% slower and needs 30-40 ms of back-to-back work to
+    reach its steady rate (per-launch events).  HIP events on the launch stream bracket exactly `reps`
     iterations; the device is synchronized before and after each batch.
     """
 
-    def __init__(self, torch, preroll_ms: float = 25.0):
+    def __init__(self, torch, preroll_ms: float = 60.0):
         self.torch = torch
         self.preroll_ms = preroll_ms
         st = torch.cuda.current_stream()
@@ -319,7 +320,7 @@ class Timer:
         host_ms = (time.perf_counter() - h0) * 1e3 / n0
         torch.cuda.synchronize()
         gpu_ms = max(e0.elapsed_time(e1) / n0, 1e-3)
-        pre = int(min(400, max(2, np.ceil(self.preroll_ms / gpu_ms))))
+        pre = int(min(3000, max(2, np.ceil(self.preroll_ms / gpu_ms))))
         spin_ms = min(3000.0, 1.5 * host_ms * (pre + reps) + 1.0)
         out = []
         for _ in range(nbatch):

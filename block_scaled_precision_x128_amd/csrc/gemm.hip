@@ -146,14 +146,28 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   const int64_t rows_a = (M - m0) < TBM ? (M - m0) : TBM;
   const int64_t rows_b = (N - n0) < TBN ? (N - n0) : TBN;
 
+  // Two-stage exact promotion: the row-block loads of step kb + 1 are issued
+  // from inside step kb's multiply loop, a few at a time, rather than all at
+  // once after the barrier.  A burst of load instructions there stalls the
+  // waves that issue it while both waves of every SIMD are converting their
+  // B operands, and the matrix cores idle; spread through the loop the loads
+  // overlap the other wave's multiplies (256x256 tiles at 4096x7168x7168: 6%
+  // faster; the 256x192 tiles, more VALU-bound, gain nothing).
+  constexpr bool kRowsInLoop = NS == 2 && PATH == PATH_EXACT && MODE == MODE_PROMOTE;
+
   // The TBM A rows and TBN B rows of a K step form one list of LDS rows,
   // 8 rows (1 KiB) per load instruction; wave w issues instructions
   // [w*LPW, w*LPW + LPW).  Lane q lands in row 8u + q/8, stored chunk q%8,
   // which holds logical chunk (q%8) ^ lds_swz(row).
   // Row 8x + q/8 has lds_swz = (q/8) ^ (x & 1), so a lane's offset inside its
-  // 8-row block is one of two per-lane values; the block itself is selected
-  // by a descriptor that starts at its first row and ends after the tile's
-  // last valid row (scalar arithmetic, no per-block vector registers).
+  // 8-row block is one of two per-lane values.  Descriptors cover only the
+  // tile's valid rows (rows past M or N read zeros).  The block is selected
+  // either by a descriptor that starts at its first row (scalar arithmetic
+  // only; the loads issued all at once after the barrier), or, where the
+  // loads are issued from inside the multiply loop, by a wave-uniform offset
+  // added to the lane's offset in one descriptor per operand (one descriptor
+  // per block kept live through the loop costs scalar registers there).
+  // Offsets stay below 256 * K <= 2^30 bytes.
   const int q8 = lane >> 3;
   const int goff_even = q8 * (int)KB + (((lane & 7) ^ q8) << 4);
   const int goff_odd = q8 * (int)KB + (((lane & 7) ^ q8 ^ 1) << 4);
@@ -162,10 +176,11 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   };
   const uint8_t* a_base = p.a + m0 * KB;
   const uint8_t* b_base = p.b + n0 * KB;
+  const __amdgpu_buffer_rsrc_t rs_a = uniform_rsrc(a_base, rows_a * KB), rs_b = uniform_rsrc(b_base, rows_b * KB);
 
   // Scale descriptors (same row ranges) and per-lane offsets of the staged scales.
   const int64_t kq = MODE == MODE_NV4 ? K / 16 : K / 32;   // scale bytes per row
-  __amdgpu_buffer_rsrc_t rssa = block_rsrc(a_base, rows_a, 0), rssb = block_rsrc(b_base, rows_b, 0);
+  __amdgpu_buffer_rsrc_t rssa = rs_a, rssb = rs_b;
   if constexpr (MODE == MODE_PROMOTE)
     rssa = uniform_rsrc(reinterpret_cast<const float*>(p.sa) + m0 * nkb, rows_a * nkb * 4);
   if constexpr (MODE == MODE_MX || FP4) {
@@ -178,16 +193,27 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   const int64_t wblk0 = n0 / 128, wblks = (n0 + rows_b + 127) / 128 - wblk0;
   const __amdgpu_buffer_rsrc_t rssw = uniform_rsrc(swb + wblk0 * nkb, MODE == MODE_PROMOTE ? wblks * nkb * 4 : 0);
 
-  auto issue_loads = [&](int kb, int buf) {
-    const int kk = kb * 128;
+  // This wave's row-block loads u0 .. u1-1 of step kb into stage buf (kb < 0:
+  // loads past every descriptor, which read nothing and fill the stage with
+  // zeros; a stage no step reads).
+  auto issue_rows = [&](int kb, int buf, int u0, int u1) {
+    const int kk = kb < 0 ? kOutOfRange : kb * 128;
 #pragma unroll
-    for (int u = 0; u < LPW; ++u) {
+    for (int u = u0; u < u1; ++u) {
       const int x = w * LPW + u;       // 8-row block of the A+B list (wave-uniform)
-      const int off = ((x & 1) ? goff_odd : goff_even) + kk;
       const bool is_a = 8 * x < TBM;   // wave-uniform: scalar selects, no branch
-      dma_to_lds<16>(block_rsrc(is_a ? a_base : b_base, is_a ? rows_a : rows_b, is_a ? x : x - TBM / 8),
-                     lds_addr(&smem[buf][8 * x * 128]), off);
+      const int xl = is_a ? x : x - TBM / 8;
+      const int goff = (x & 1) ? goff_odd : goff_even;
+      if constexpr (kRowsInLoop)
+        dma16_to_lds_add(is_a ? rs_a : rs_b, lds_addr(&smem[buf][8 * x * 128]), goff,
+                         __builtin_amdgcn_readfirstlane(xl * 8 * (int)KB + kk));
+      else
+        dma_to_lds<16>(block_rsrc(is_a ? a_base : b_base, is_a ? rows_a : rows_b, xl),
+                       lds_addr(&smem[buf][8 * x * 128]), goff + kk);
     }
+  };
+  auto issue_loads = [&](int kb, int buf, bool rows) {
+    if (rows) issue_rows(kb, buf, 0, LPW);
     // Scales, 64 rows per 4-byte load, spread so that every wave issues
     // exactly SC of them per step (a wave with no chunk left loads zeros into
     // a spare slot): every wave then issues the same number of loads per
@@ -273,7 +299,8 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
 
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (j < nkb) issue_loads(j, j);
+    if (j < nkb) issue_loads(j, j, true);
+
 
   // Wait for step kb's loads (those of later steps stay in flight: every wave
   // issues LOADS per step, and loads complete in issue order), publish the
@@ -293,7 +320,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
-    if (kb + NS - 1 < nkb) issue_loads(kb + NS - 1, buf == 0 ? NS - 1 : buf - 1);
+    if (kb + NS - 1 < nkb) issue_loads(kb + NS - 1, buf == 0 ? NS - 1 : buf - 1, !kRowsInLoop);
   };
 
   int buf = 0;   // stage of step kb
@@ -466,6 +493,14 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         xa[3] = cvt8<AF>(n1.z, n1.w, 1.0f);
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
+          if constexpr (kRowsInLoop) {
+            // step kb + 1's row blocks, spread over the odd i (the last step
+            // issues filler loads: no branch inside the unrolled loop, which
+            // measured to cost register spills)
+            if (i & 1)
+              issue_rows(kb + 1 < nkb ? kb + 1 : -1, buf ^ 1, (i >> 1) * LPW / (MI / 2),
+                         ((i >> 1) + 1) * LPW / (MI / 2));
+          }
           if (i + 1 < MI) {
             const int r = a_row0 + 16 * (i + 1);
             n0 = lds16(sa_, r * 128 + c0);
@@ -526,6 +561,9 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
     }
     buf = buf + 1 == NS ? 0 : buf + 1;
   }
+  // the last step's filler loads still write LDS: drain them before the
+  // workgroup can exit
+  if constexpr (kRowsInLoop) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if constexpr (MX_WORDS) {
     // Block-by-block exact MX: one 32-K block b of the step per instruction,

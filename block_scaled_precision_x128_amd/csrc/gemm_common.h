@@ -72,6 +72,20 @@ __device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t l
                  : "memory");
 }
 
+// dma_to_lds<16> at buffer offset voff + soff (soff wave-uniform), the sum
+// formed inside the same assembly block: a kernel that issues many such loads
+// from per-lane bases it keeps for the whole loop then holds no per-load
+// offset registers (the compiler would otherwise keep each sum live across
+// the loop).  Offsets add modulo 2^32; a sum at or past the descriptor's size
+// writes zeros.
+__device__ __forceinline__ void dma16_to_lds_add(__amdgpu_buffer_rsrc_t rs, uint32_t lds_base, int voff, int soff) {
+  int sum;
+  asm volatile("v_add_u32 %0, %1, %2\n\ts_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %4, 0 offen lds"
+               : "=&v"(sum)
+               : "s"(soff), "v"(voff), "s"(lds_base), "s"(rs)
+               : "memory");
+}
+
 template <int AF, int BF>
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AF, BF, 0, sa, 0, sb);
