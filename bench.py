@@ -275,6 +275,46 @@ def summarize_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, kern
     return "\n".join(lines)
 
 
+def summarize_counters(csv_paths, kernel_re, sources=GEMM_SOURCES) -> str:
+    """Per-kernel means over dispatches of every counter found in the given
+    rocprofv3 --pmc CSV files (one pass each), and the figures derived from
+    them: instructions per wave and per MFMA instruction."""
+    import csv
+    import re
+    pat = re.compile(kernel_re)
+    vals = {}   # kernel -> counter -> [values]
+    grids = {}
+    for path in csv_paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                n = r.get("Kernel_Name", "")
+                if not pat.search(n):
+                    continue
+                vals.setdefault(n, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                grids[n] = int(float(r.get("Grid_Size") or 0))
+    if not vals:
+        raise SystemExit("no dispatch of the selected kernels in " + ", ".join(csv_paths))
+    lines = [f"kernel_match: {kernel_re}"]
+    for n in sorted(vals):
+        c = {k: float(np.mean(v)) for k, v in vals[n].items()}
+        waves = grids[n] / 64.0
+        lines.append(f"kernel {n}  (grid {grids[n]} threads = {waves:.0f} waves)")
+        for k in sorted(c):
+            lines.append(f"  {k}: {c[k]:.6g}   ({len(vals[n][k])} dispatches)")
+        mf = c.get("SQ_INSTS_MFMA")
+        if mf:
+            for k in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_CVT", "SQ_INSTS_VALU_FMA_F32", "SQ_INSTS_VALU_MUL_F32",
+                      "SQ_INSTS_LDS", "SQ_INSTS_VMEM", "SQ_INSTS_SALU"):
+                if k in c:
+                    lines.append(f"  per MFMA instruction {k}: {c[k] / mf:.3f}")
+            if "SQ_INSTS_VALU" in c:
+                lines.append(f"  per MFMA instruction non-MFMA VALU: {(c['SQ_INSTS_VALU'] - mf) / mf:.3f}"
+                             "   (SQ_INSTS_VALU counts the MFMAs too)")
+            lines.append(f"  MFMA instructions per wave: {mf / waves:.1f}")
+    lines.append(f"source_sha256: {gemm_source_hash(sources)}")
+    return "\n".join(lines)
+
+
 # ---- timing -------------------------------------------------------------------
 
 class Timer:
@@ -718,12 +758,21 @@ def main(argv=None) -> int:
                     help="kernel-name regular expression for --summarize-traffic")
     ap.add_argument("--traffic-sources", choices=["gemm", "kv"], default="gemm",
                     help="which kernel sources the --summarize-traffic hash covers")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="print per-kernel means of the counters in these rocprofv3 --pmc CSV files and exit")
+    ap.add_argument("--preroll-ms", type=float, default=60.0,
+                    help="untimed back-to-back work before each timed batch (clock ramp)")
+    ap.add_argument("--profile-gemm", type=int, default=0, metavar="N",
+                    help="only run the workload's GEMM N times on its bench inputs (for rocprofv3 --pmc runs)")
     ap.add_argument("--min-grid", type=int, default=0,
                     help="--summarize-traffic: only dispatches of at least this many threads")
     args = ap.parse_args(argv)
 
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
+        return 0
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, args.kernel_match))
         return 0
     if args.summarize_traffic:
         print(summarize_traffic(*args.summarize_traffic, args.kernel_match, COPY_PROBE_BYTES,
@@ -762,7 +811,9 @@ def main(argv=None) -> int:
 
     wl = workloads.CONFIGS[args.workload]
     accum = fb.ACCUM_NATIVE if args.accum == "native" else fb.ACCUM_FP32
-    timer = Timer(torch)
+    if args.profile_gemm:
+        return profile_gemm(torch, fb, wl, accum, args.profile_gemm)
+    timer = Timer(torch, preroll_ms=args.preroll_ms)
     head = fp8_workload(torch, fb, timer, wl, args, accum, headline=True)
     result = head.pop("result")
 
@@ -783,6 +834,30 @@ def main(argv=None) -> int:
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, min(args.cpu_sample_rows, wl.M))
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def profile_gemm(torch, fb, wl, accum, n: int) -> int:
+    """The workload's GEMM alone, n launches on the bench's inputs (quantized
+    by the library), for counter runs."""
+    dev = torch.device("cuda:0")
+    xs_np, ws_np = workloads.make_inputs(wl)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    xq, sx = fb.fp8_quantize(to_dev(xs_np), wl.x_fmt, wl.x_gran)
+    wq, sw = fb.fp8_quantize(to_dev(ws_np), wl.w_fmt, wl.w_gran)
+    out = torch.empty((wl.M, wl.N), dtype=torch.bfloat16 if wl.out_dtype == fb.DT_BF16 else torch.float32,
+                      device=dev)
+    for _ in range(n):
+        fb.fp8_gemm_blockscaled(xq, wl.x_fmt, wl.x_gran, sx, wq, wl.w_fmt, wl.w_gran, sw, wl.out_dtype, out=out,
+                                accum=accum)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_gemm": wl.name, "launches": n, "accum": "native" if accum == fb.ACCUM_NATIVE
+                      else "fp32"}), flush=True)
     return 0
 
 

@@ -284,6 +284,14 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // When a wave's columns can straddle a 128-column block (WC does not divide
   // 128), each lane takes the W block scale of its own column, per N tile.
   constexpr bool kWaveWScale = (128 % WC) == 0;
+  // Exact promotion with such waves: the products are formed transposed (W
+  // rows as the instruction's first operand), so a lane holds one output row
+  // and four consecutive columns of each N tile; a 16-column tile never
+  // straddles a 128-column block, so the scale of a lane's N tile is one
+  // product sA * sB instead of four (256x192 tiles at 4096x7168x7168: one
+  // multiply per MFMA instruction fewer, measured with SQ_INSTS_VALU_MUL_F32).
+  constexpr bool kTransposed = !kWaveWScale && PATH == PATH_EXACT && MODE == MODE_PROMOTE;
+  static_assert(!kTransposed || ODT < ODT_Q_E4M3, "the quantized epilogue takes the untransposed layout");
   int jblk[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -506,8 +514,16 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
             n0 = lds16(sa_, r * 128 + c0);
             n1 = lds16(sa_, r * 128 + c1);
           }
-          const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * WR + 16 * i + 4 * g]);
-          const v4f sc = {sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};  // swv = 1 when per lane
+          // Scales of this A tile's rows, read before the multiplies: untransposed,
+          // lane rows 16 i + 4 g + q; transposed, lane row 16 i + l%16.
+          v4f sc = {0.0f, 0.0f, 0.0f, 0.0f};
+          float sxl = 0.0f;
+          if constexpr (kTransposed) {
+            sxl = s_x[buf][wm * WR + 16 * i + (lane & 15)];
+          } else {
+            const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * WR + 16 * i + 4 * g]);
+            sc = v4f{sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};  // swv = 1 when per lane
+          }
           // Four independent chains (one per N tile), interleaved so that
           // no MFMA waits on the previous one; the wave's priority is raised
           // while it issues them so that a co-resident wave's VALU work fills
@@ -515,16 +531,32 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
           __builtin_amdgcn_s_setprio(1);
           v4f pp[NJ];
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) pp[j] = mfma_bf16(xa[0], xb[j][0], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+          for (int j = 0; j < NJ; ++j)
+            pp[j] = kTransposed ? mfma_bf16(xb[j][0], xa[0], v4f{0.0f, 0.0f, 0.0f, 0.0f})
+                                : mfma_bf16(xa[0], xb[j][0], v4f{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
           for (int s = 1; s < 4; ++s)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) pp[j] = mfma_bf16(xa[s], xb[j][s], pp[j]);
+            for (int j = 0; j < NJ; ++j)
+              pp[j] = kTransposed ? mfma_bf16(xb[j][s], xa[s], pp[j]) : mfma_bf16(xa[s], xb[j][s], pp[j]);
           __builtin_amdgcn_s_setprio(0);
+          if constexpr (kTransposed) {
+            // lane: output row 16 i + l%16 (one sA), columns 16 j + 4 g + q
+            // (one W block per N tile): one scale per N tile
 #pragma unroll
-          for (int j = 0; j < NJ; ++j)
+            for (int j = 0; j < NJ; ++j) {
+              const float scj = sxl * swj[j];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(pp[j][q], kWaveWScale ? sc[q] : sc[q] * swj[j], acc[i][j][q]);
+              for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(pp[j][q], scj, acc[i][j][q]);
+            }
+          } else {
+            // lane: output rows 16 i + 4 g + q, column 16 j + l%16
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                acc[i][j][q] = __builtin_fmaf(pp[j][q], kWaveWScale ? sc[q] : sc[q] * swj[j], acc[i][j][q]);
+          }
           if (i + 1 < MI) {
             xa[0] = cvt8<AF>(n0.x, n0.y, 1.0f);
             xa[1] = cvt8<AF>(n0.z, n0.w, 1.0f);
@@ -664,6 +696,20 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
           for (int j = 0; j < NJ; ++j) o[16 * j] = (uint8_t)(codes >> (8 * j));
           if ((wn & 1) == 0 && (lane & 15) == 0) p.out_scales[row * nsg + grp] = s;
         }
+      }
+    }
+  } else if constexpr (kTransposed) {
+    // lane: row 16 i + l%16, columns 16 j + 4 g + q (N is a multiple of 16,
+    // so an N tile is stored whole or not at all)
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int64_t row = m0 + wm * WR + i * 16 + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int64_t cbase = n0 + wn * WC + j * 16;
+        if (row >= M || cbase >= N) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) store_out<ODT>(p.out, row * p.ldo + cbase + 4 * g + q, acc[i][j][q]);
       }
     }
   } else {
