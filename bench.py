@@ -442,6 +442,56 @@ def measure_ceilings(torch, fb, timer, reps: int):
     return res
 
 
+class SizedCeilings:
+    """The read and copy probes at the byte volume of a given kernel, so that a
+    kernel moving tens of megabytes is priced against what a plain stream of
+    the same size reaches (launch, ramp-up and drain weigh more there than in
+    the 1 GiB figures).  Each iteration takes the next disjoint slice of two
+    1 GiB buffers, so the slices cycled over exceed the 256 MB last-level
+    cache as the kernels' rotated input sets do.  copy: half the bytes read,
+    half written (the quantize and dequantize kernels read 2:1 or 1:2)."""
+
+    def __init__(self, torch, fb, timer, reps: int):
+        self.fb, self.timer, self.reps = fb, timer, max(5, reps)
+        self.src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(3)
+        self.dst = torch.empty_like(self.src)
+        self.sink = torch.empty(int(fb.load_library().fp8blk_probe_read_sink_floats()), dtype=torch.float32,
+                                device="cuda")
+        self.cache = {}
+
+    def gbs(self, kind: str, total_bytes: int) -> float:
+        n = (total_bytes // 2 if kind == "copy" else total_bytes) // 4096 * 4096
+        n = max(4096, min(n, 1 << 30))
+        if (kind, n) not in self.cache:
+            slots = max(1, (1 << 30) // n)
+            src, dst, sink, fb = self.src, self.dst, self.sink, self.fb
+            if kind == "copy":
+                f = lambda i, st: fb.probe_copy(src[(i % slots) * n:(i % slots + 1) * n],
+                                                dst[(i % slots) * n:(i % slots + 1) * n], stream=st)
+            else:
+                f = lambda i, st: fb.probe_read(src[(i % slots) * n:(i % slots + 1) * n], sink, stream=st)
+            ms = median(self.timer.batches(f, self.reps))
+            self.cache[(kind, n)] = (2 if kind == "copy" else 1) * n / (ms * 1e-3) / 1e9
+        return self.cache[(kind, n)]
+
+    def annotate(self, kern: dict, wl):
+        """Adds <kernel>_ceiling_gbs and <kernel>_frac_ceiling for the
+        HBM-bound kernels of a workload's figures."""
+        items = [("quantize_x", quant_bytes(wl, "x"), "copy"), ("quantize_w", quant_bytes(wl, "w"), "copy"),
+                 ("dequantize_x", dequant_bytes(wl), "copy")]
+        if "quantize_x_delayed_gbs" in kern:
+            in_b = 2 if wl.in_dtype == workloads.DT_BF16 else 4
+            items.append(("quantize_x_delayed", wl.M * wl.K * (in_b + 1) + 8, "copy"))
+        for key, nbytes, kind in items:
+            g = self.gbs(kind, nbytes)
+            kern[f"{key}_ceiling_gbs"] = round(g, 1)
+            kern[f"{key}_frac_ceiling"] = round(kern[f"{key}_gbs"] / g, 4)
+        if wl.M <= 64:   # decode: the GEMM streams W once
+            g = self.gbs("read", gemm_bytes(wl))
+            kern["gemm_ceiling_gbs"] = round(g, 1)
+            kern["gemm_frac_ceiling"] = round(kern["gemm_algorithmic_gbs"] / g, 4)
+
+
 # ---- FP8 KV cache ----------------------------------------------------------
 
 def kv_bytes(wl, op: str) -> int:
@@ -829,6 +879,16 @@ def main(argv=None) -> int:
         result["configs"] = others
     if not args.no_ceilings:
         result["ceilings"] = measure_ceilings(torch, fb, timer, args.steps)
+        # HBM-bound kernels against a read or copy of their own byte volume
+        sized = SizedCeilings(torch, fb, timer, args.steps)
+        sized.annotate(result["kernels"], wl)
+        for name, kern in result.get("configs", {}).items():
+            sized.annotate(kern, workloads.CONFIGS[name])
+        result["ceilings"]["sized_note"] = ("<kernel>_ceiling_gbs: the read probe (decode GEMM) or the copy probe "
+                                            "(quantize, dequantize; half the bytes read, half written) moving the "
+                                            "kernel's own byte volume, over disjoint slices of 1 GiB buffers")
+        del sized
+        torch.cuda.empty_cache()
         torch.cuda.empty_cache()
     result["gpu_clocks"] = gpu_clocks()
     if not args.no_cpu_baseline:
