@@ -325,7 +325,7 @@ class Timer:
     that keeps the GPU busy while the host queues the launches, so the timed
     launches run back to back with no host gaps; between the spin and the
     timed launches sits an untimed pre-roll of the same work lasting at least
-    `preroll_ms` (at most 3000 iterations), so the timed launches start at the
+    `preroll_ms` (at most 1000 iterations), so the timed launches start at the
     engine clock a sustained load runs at: after a spin or an idle host the
     c3 GEMM starts about 20% slower and needs 30-40 ms of back-to-back work to
     reach its steady rate (per-launch events).  HIP events on the launch stream bracket exactly `reps`
@@ -360,7 +360,11 @@ class Timer:
         host_ms = (time.perf_counter() - h0) * 1e3 / n0
         torch.cuda.synchronize()
         gpu_ms = max(e0.elapsed_time(e1) / n0, 1e-3)
-        pre = int(min(3000, max(2, np.ceil(self.preroll_ms / gpu_ms))))
+        # at most 1000 pre-roll launches: queued work past the stream's hardware
+        # queue blocks the host, and a kernel shorter than its own launch cost
+        # then runs at the host's enqueue rate (a 4.8 us KV decode append
+        # measured 23.5 us with 3000)
+        pre = int(min(1000, max(2, np.ceil(self.preroll_ms / gpu_ms))))
         spin_ms = min(3000.0, 1.5 * host_ms * (pre + reps) + 1.0)
         out = []
         for _ in range(nbatch):
@@ -564,7 +568,7 @@ def bench_kv(args, wl) -> int:
     for i in range(args.warmup):
         step(i, stream)
     torch.cuda.synchronize()
-    timer = Timer(torch)
+    timer = Timer(torch, preroll_ms=args.preroll_ms)
     wall0 = time.perf_counter()
     step_batches = timer.batches(step, args.steps)
     wall = time.perf_counter() - wall0
@@ -721,7 +725,7 @@ def bench_fp4(args, wl) -> int:
     for i in range(args.warmup):
         step(i, stream)
     torch.cuda.synchronize()
-    timer = Timer(torch)
+    timer = Timer(torch, preroll_ms=args.preroll_ms)
     wall0 = time.perf_counter()
     step_batches = timer.batches(step, args.steps)
     wall = time.perf_counter() - wall0
