@@ -291,6 +291,8 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // product sA * sB instead of four (256x192 tiles at 4096x7168x7168: one
   // multiply per MFMA instruction fewer, measured with SQ_INSTS_VALU_MUL_F32).
   constexpr bool kTransposed = !kWaveWScale && PATH == PATH_EXACT && MODE == MODE_PROMOTE;
+  // Exact promotion on wave tiles wider than tall: A held for the step, B streamed.
+  constexpr bool kStreamB = kTransposed && NJ > MI;
   static_assert(!kTransposed || ODT < ODT_Q_E4M3, "the quantized epilogue takes the untransposed layout");
   int jblk[NJ];
 #pragma unroll
@@ -473,6 +475,72 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
           for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int j = 0; j < NJ; ++j) acc[i][j] = mma(xa[s], xb[j][s], acc[i][j]);
+        }
+      }
+    } else if constexpr (kStreamB) {
+      // Exact promotion with A held for the step (wave tiles wider than they
+      // are tall): the MI A tiles are converted once after the barrier, then
+      // N tile j is read and converted while tile j-1 multiplies.  Products
+      // transposed (kTransposed): lane l holds output row 16 i + l%16 and
+      // columns 16 j + 4 g + q, so one sA * sB per (i, j).
+      v8bf xa[MI][4];
+      float sxl[MI];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int r = a_row0 + 16 * i;
+        const u32x4 d0 = lds16(sa_, r * 128 + c0), d1 = lds16(sa_, r * 128 + c1);
+        xa[i][0] = cvt8<AF>(d0.x, d0.y, 1.0f);
+        xa[i][1] = cvt8<AF>(d0.z, d0.w, 1.0f);
+        xa[i][2] = cvt8<AF>(d1.x, d1.y, 1.0f);
+        xa[i][3] = cvt8<AF>(d1.z, d1.w, 1.0f);
+        sxl[i] = s_x[buf][wm * WR + 16 * i + (lane & 15)];
+      }
+      u32x4 n0 = lds16(sb_, b_row0 * 128 + c0), n1 = lds16(sb_, b_row0 * 128 + c1);
+      v8bf xbv[4];
+      xbv[0] = cvt8<BF>(n0.x, n0.y, 1.0f);
+      xbv[1] = cvt8<BF>(n0.z, n0.w, 1.0f);
+      xbv[2] = cvt8<BF>(n1.x, n1.y, 1.0f);
+      xbv[3] = cvt8<BF>(n1.z, n1.w, 1.0f);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if constexpr (kRowsInLoop) {
+          // step kb + 1's row blocks, spread over the odd N tiles (filler
+          // loads on the last step: no branch in the unrolled loop)
+          if (j & 1)
+            issue_rows(kb + 1 < nkb ? kb + 1 : -1, buf ^ 1, (j >> 1) * LPW / (NJ / 2),
+                       ((j >> 1) + 1) * LPW / (NJ / 2));
+        }
+        if (j + 1 < NJ) {
+          const int r = b_row0 + 16 * (j + 1);
+          n0 = lds16(sb_, r * 128 + c0);
+          n1 = lds16(sb_, r * 128 + c1);
+        }
+        __builtin_amdgcn_s_setprio(1);
+        v4f pp[MI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i) pp[i] = mfma_bf16(xbv[0], xa[i][0], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+        for (int s = 1; s < 4; ++s)
+#pragma unroll
+          for (int i = 0; i < MI; ++i) pp[i] = mfma_bf16(xbv[s], xa[i][s], pp[i]);
+        __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const float sc = sxl[i] * swj[j];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(pp[i][q], sc, acc[i][j][q]);
+        }
+        if (j + 1 < NJ) {
+          xbv[0] = cvt8<BF>(n0.x, n0.y, 1.0f);
+          xbv[1] = cvt8<BF>(n0.z, n0.w, 1.0f);
+          xbv[2] = cvt8<BF>(n1.x, n1.y, 1.0f);
+          xbv[3] = cvt8<BF>(n1.z, n1.w, 1.0f);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int z = 0; z < 4 * MI; ++z) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
       }
     } else {
@@ -749,7 +817,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_tiled_256x256(GemmArgs p) {
 }
 template <int AF, int BF, int MODE, int ODT, int PATH>
 __global__ __launch_bounds__(512, 1) void k_gemm_tiled_256x192(GemmArgs p) {
-  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 8, 3, 2>(p);
+  if constexpr (MODE == MODE_PROMOTE && PATH == PATH_EXACT)
+    gemm_tiled_body<AF, BF, MODE, ODT, PATH, 4, 2, 4, 6, 2>(p);   // 64x96 wave tiles, A held, B streamed
+  else
+    gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 8, 3, 2>(p);
 }
 // (NVFP4 stages 16 scale bytes per row and step: three stages would exceed
 // the 160 KiB of LDS, so it runs two.)
