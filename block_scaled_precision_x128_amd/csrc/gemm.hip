@@ -291,8 +291,10 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // product sA * sB instead of four (256x192 tiles at 4096x7168x7168: one
   // multiply per MFMA instruction fewer, measured with SQ_INSTS_VALU_MUL_F32).
   constexpr bool kTransposed = !kWaveWScale && PATH == PATH_EXACT && MODE == MODE_PROMOTE;
-  // Exact promotion on wave tiles wider than tall: A held for the step, B streamed.
+  // Exact promotion on wave tiles wider than tall: A held for the step, B streamed
+  // (the only layout that takes the transposed products).
   constexpr bool kStreamB = kTransposed && NJ > MI;
+  static_assert(!kTransposed || kStreamB, "transposed products are formed by the streamed-B loop only");
   static_assert(!kTransposed || ODT < ODT_Q_E4M3, "the quantized epilogue takes the untransposed layout");
   int jblk[NJ];
 #pragma unroll
@@ -480,7 +482,8 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
     } else if constexpr (kStreamB) {
       // Exact promotion with A held for the step (wave tiles wider than they
       // are tall): the MI A tiles are converted once after the barrier, then
-      // N tile j is read and converted while tile j-1 multiplies.  Products
+      // N tile j+1 is read and converted, and tile j-1's partials promoted,
+      // while tile j multiplies (the deferred promotion measured 1.8% faster).  Products
       // transposed (kTransposed): lane l holds output row 16 i + l%16 and
       // columns 16 j + 4 g + q, so one sA * sB per (i, j).
       v8bf xa[MI][4];
@@ -497,6 +500,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       }
       u32x4 n0 = lds16(sb_, b_row0 * 128 + c0), n1 = lds16(sb_, b_row0 * 128 + c1);
       v8bf xbv[4];
+      v4f ppd[MI];   // the previous N tile's partials, promoted under this tile's MFMAs
       xbv[0] = cvt8<BF>(n0.x, n0.y, 1.0f);
       xbv[1] = cvt8<BF>(n0.z, n0.w, 1.0f);
       xbv[2] = cvt8<BF>(n1.x, n1.y, 1.0f);
@@ -524,12 +528,16 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
 #pragma unroll
           for (int i = 0; i < MI; ++i) pp[i] = mfma_bf16(xbv[s], xa[i][s], pp[i]);
         __builtin_amdgcn_s_setprio(0);
+        if (j > 0) {
 #pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          const float sc = sxl[i] * swj[j];
+          for (int i = 0; i < MI; ++i) {
+            const float sc = sxl[i] * swj[j - 1];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(pp[i][q], sc, acc[i][j][q]);
+            for (int q = 0; q < 4; ++q) acc[i][j - 1][q] = __builtin_fmaf(ppd[i][q], sc, acc[i][j - 1][q]);
+          }
         }
+#pragma unroll
+        for (int i = 0; i < MI; ++i) ppd[i] = pp[i];
         if (j + 1 < NJ) {
           xbv[0] = cvt8<BF>(n0.x, n0.y, 1.0f);
           xbv[1] = cvt8<BF>(n0.z, n0.w, 1.0f);
@@ -542,6 +550,12 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const float sc = sxl[i] * swj[NJ - 1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][NJ - 1][q] = __builtin_fmaf(ppd[i][q], sc, acc[i][NJ - 1][q]);
       }
     } else {
       // Exact path: four K=32 sub-steps on bf16 operands (MX scales folded in).
@@ -582,16 +596,9 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
             n0 = lds16(sa_, r * 128 + c0);
             n1 = lds16(sa_, r * 128 + c1);
           }
-          // Scales of this A tile's rows, read before the multiplies: untransposed,
-          // lane rows 16 i + 4 g + q; transposed, lane row 16 i + l%16.
-          v4f sc = {0.0f, 0.0f, 0.0f, 0.0f};
-          float sxl = 0.0f;
-          if constexpr (kTransposed) {
-            sxl = s_x[buf][wm * WR + 16 * i + (lane & 15)];
-          } else {
-            const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * WR + 16 * i + 4 * g]);
-            sc = v4f{sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};  // swv = 1 when per lane
-          }
+          // scales of this A tile's rows (lane rows 16 i + 4 g + q), read before the multiplies
+          const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * WR + 16 * i + 4 * g]);
+          const v4f sc = {sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};  // swv = 1 when per lane
           // Four independent chains (one per N tile), interleaved so that
           // no MFMA waits on the previous one; the wave's priority is raised
           // while it issues them so that a co-resident wave's VALU work fills
@@ -599,32 +606,18 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
           __builtin_amdgcn_s_setprio(1);
           v4f pp[NJ];
 #pragma unroll
-          for (int j = 0; j < NJ; ++j)
-            pp[j] = kTransposed ? mfma_bf16(xb[j][0], xa[0], v4f{0.0f, 0.0f, 0.0f, 0.0f})
-                                : mfma_bf16(xa[0], xb[j][0], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+          for (int j = 0; j < NJ; ++j) pp[j] = mfma_bf16(xa[0], xb[j][0], v4f{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
           for (int s = 1; s < 4; ++s)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
-              pp[j] = kTransposed ? mfma_bf16(xb[j][s], xa[s], pp[j]) : mfma_bf16(xa[s], xb[j][s], pp[j]);
+            for (int j = 0; j < NJ; ++j) pp[j] = mfma_bf16(xa[s], xb[j][s], pp[j]);
           __builtin_amdgcn_s_setprio(0);
-          if constexpr (kTransposed) {
-            // lane: output row 16 i + l%16 (one sA), columns 16 j + 4 g + q
-            // (one W block per N tile): one scale per N tile
+          // lane: output rows 16 i + 4 g + q, column 16 j + l%16
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-              const float scj = sxl * swj[j];
+          for (int j = 0; j < NJ; ++j)
 #pragma unroll
-              for (int q = 0; q < 4; ++q) acc[i][j][q] = __builtin_fmaf(pp[j][q], scj, acc[i][j][q]);
-            }
-          } else {
-            // lane: output rows 16 i + 4 g + q, column 16 j + l%16
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                acc[i][j][q] = __builtin_fmaf(pp[j][q], kWaveWScale ? sc[q] : sc[q] * swj[j], acc[i][j][q]);
-          }
+            for (int q = 0; q < 4; ++q)
+              acc[i][j][q] = __builtin_fmaf(pp[j][q], kWaveWScale ? sc[q] : sc[q] * swj[j], acc[i][j][q]);
           if (i + 1 < MI) {
             xa[0] = cvt8<AF>(n0.x, n0.y, 1.0f);
             xa[1] = cvt8<AF>(n0.z, n0.w, 1.0f);
