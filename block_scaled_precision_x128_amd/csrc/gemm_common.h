@@ -64,6 +64,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 template <int SIZE>
 __device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t lds_base, int voff) {
   static_assert(SIZE == 16 || SIZE == 4, "16- or 4-byte loads");
+  // wave-uniform by contract; read from the first lane so that the compiler
+  // places it in a scalar register even where it cannot prove uniformity
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);
   if constexpr (SIZE == 16)
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "s"(lds_base)
                  : "memory");
@@ -79,6 +82,8 @@ __device__ __forceinline__ void dma_to_lds(__amdgpu_buffer_rsrc_t rs, uint32_t l
 // the loop).  Offsets add modulo 2^32; a sum at or past the descriptor's size
 // writes zeros.
 __device__ __forceinline__ void dma16_to_lds_add(__amdgpu_buffer_rsrc_t rs, uint32_t lds_base, int voff, int soff) {
+  lds_base = __builtin_amdgcn_readfirstlane(lds_base);   // wave-uniform by contract (as dma_to_lds)
+  soff = __builtin_amdgcn_readfirstlane(soff);
   int sum;
   asm volatile("v_add_u32 %0, %1, %2\n\ts_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %4, 0 offen lds"
                : "=&v"(sum)
