@@ -423,6 +423,11 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         fb[j] = join(lds16(sb_, r * 128 + c0), lds16(sb_, r * 128 + c1));
         if constexpr (MODE == MODE_MX) eb[j] = (int)((s_e[buf][0][TBM + r] >> (8 * g)) & 0xffu);
       }
+      // Outside promotion the next A fragment is read one tile ahead (MX: 2.6%
+      // faster at c5; with promotion it measured 2.7% slower at c3).
+      constexpr bool kPrefetchA = MODE != MODE_PROMOTE;
+      v8i fa_next = {};
+      if constexpr (kPrefetchA) fa_next = join(lds16(sa_, a_row0 * 128 + c0), lds16(sa_, a_row0 * 128 + c1));
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         if constexpr (kRowsInLoop) {
@@ -431,7 +436,13 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
                        ((i >> 1) + 1) * LPW / (MI / 2));
         }
         const int r = a_row0 + 16 * i;
-        const v8i fa = join(lds16(sa_, r * 128 + c0), lds16(sa_, r * 128 + c1));
+        v8i fa;
+        if constexpr (kPrefetchA) {
+          fa = fa_next;
+          if (i + 1 < MI) fa_next = join(lds16(sa_, (r + 16) * 128 + c0), lds16(sa_, (r + 16) * 128 + c1));
+        } else {
+          fa = join(lds16(sa_, r * 128 + c0), lds16(sa_, r * 128 + c1));
+        }
         if constexpr (MODE == MODE_PROMOTE) {
           const float4 sx4 = *reinterpret_cast<const float4*>(&s_x[buf][wm * WR + 16 * i + 4 * g]);
           const v4f sc = {sx4.x * swv, sx4.y * swv, sx4.z * swv, sx4.w * swv};  // swv = 1 when per lane
