@@ -325,7 +325,7 @@ class Timer:
     that keeps the GPU busy while the host queues the launches, so the timed
     launches run back to back with no host gaps; between the spin and the
     timed launches sits an untimed pre-roll of the same work lasting at least
-    `preroll_ms` (at most 1000 iterations), so the timed launches start at the
+    `preroll_ms` (at most 400 iterations), so the timed launches start at the
     engine clock a sustained load runs at: after a spin or an idle host the
     c3 GEMM starts about 20% slower and needs 30-40 ms of back-to-back work to
     reach its steady rate (per-launch events).  HIP events on the launch stream bracket exactly `reps`
@@ -360,11 +360,12 @@ class Timer:
         host_ms = (time.perf_counter() - h0) * 1e3 / n0
         torch.cuda.synchronize()
         gpu_ms = max(e0.elapsed_time(e1) / n0, 1e-3)
-        # at most 1000 pre-roll launches: queued work past the stream's hardware
-        # queue blocks the host, and a kernel shorter than its own launch cost
-        # then runs at the host's enqueue rate (a 4.8 us KV decode append
-        # measured 23.5 us with 3000)
-        pre = int(min(1000, max(2, np.ceil(self.preroll_ms / gpu_ms))))
+        # at most 400 pre-roll iterations: queued work past the stream's hardware
+        # queue blocks the host, and work shorter than its own launch cost then
+        # runs at the host's enqueue rate (a 4.8 us KV decode append measured
+        # 23.5 us with 3000 iterations; c1's two-launch per-tensor quantize,
+        # 8 us of GPU time, measured 19 us with 1000)
+        pre = int(min(400, max(2, np.ceil(self.preroll_ms / gpu_ms))))
         spin_ms = min(3000.0, 1.5 * host_ms * (pre + reps) + 1.0)
         out = []
         for _ in range(nbatch):
