@@ -780,6 +780,21 @@ def bench_fp4(args, wl) -> int:
         "step_batches_ms": [round(x, 4) for x in step_batches],
         "wall_s_timed": round(wall, 4),
     }
+    if not args.no_ceilings:
+        # the HBM-bound kernels against a read or copy of their own byte volume
+        sized = SizedCeilings(torch, fb, timer, args.steps)
+        kern = result["kernels"]
+        items = [("quantize_x", qbytes(M), "copy"), ("quantize_w", qbytes(N), "copy"),
+                 ("dequantize_x", M * K // 2 + M * (K // blk) + M * K * 2, "copy")]
+        for key, nbytes, how in items:
+            g = sized.gbs(how, nbytes)
+            kern[f"{key}_ceiling_gbs"] = round(g, 1)
+            kern[f"{key}_frac_ceiling"] = round(kern[f"{key}_gbs"] / g, 4)
+        if decode:
+            g = sized.gbs("read", fp4_gemm_bytes(wl))
+            kern["gemm_ceiling_gbs"] = round(g, 1)
+            kern["gemm_frac_ceiling"] = round(gemm_gbs / g, 4)
+        del sized
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = fp4_cpu_baseline(wl, min(1024, M), 4096)
     print(json.dumps(result), flush=True)
