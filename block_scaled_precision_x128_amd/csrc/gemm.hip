@@ -210,10 +210,10 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       const int goff = (x & 1) ? goff_odd : goff_even;
       if constexpr (kRowsInLoop)
         dma16_to_lds_add(is_a ? rs_a : rs_b, lds_addr(&smem[buf][8 * x * 128]), goff,
-                         __builtin_amdgcn_readfirstlane(xl * 8 * (int)KB + kk));
+                         __builtin_amdgcn_readfirstlane(off_add(xl * 8 * (int)KB, kk)));
       else
         dma_to_lds<16>(block_rsrc(is_a ? a_base : b_base, is_a ? rows_a : rows_b, xl),
-                       lds_addr(&smem[buf][8 * x * 128]), goff + kk);
+                       lds_addr(&smem[buf][8 * x * 128]), off_add(goff, kk));
     }
   };
   auto issue_loads = [&](int kb, int buf, bool rows) {

@@ -188,6 +188,10 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
 // return zeros without touching memory.
 constexpr int kOutOfRange = 0x7ff00000;
 
+// Byte offset a + b modulo 2^32, as the buffer unit adds them: a valid offset
+// plus kOutOfRange can pass INT_MAX, and stays past every descriptor's range.
+__device__ __forceinline__ int off_add(int a, int b) { return (int)((uint32_t)a + (uint32_t)b); }
+
 // Compute units of the current device (cached per device).
 inline int num_cus() {
   static int cus[64] = {0};

@@ -108,25 +108,25 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
 #pragma unroll
     for (int u = 0; u < 2 * T; ++u) {
       const int64_t left = rows - 8 * u;
-      dma_to_lds<16>(rsrc(wbase + 8 * u * K, left * K), lds_addr(st + 8 * u * 128), ((u & 1) ? off_odd : off_even) + kk);
+      dma_to_lds<16>(rsrc(wbase + 8 * u * K, left * K), lds_addr(st + 8 * u * 128), off_add((u & 1) ? off_odd : off_even, kk));
     }
 #pragma unroll
     for (int u = 0; u < 2 * MT; ++u) {
       const int64_t left = M - 8 * u;
       dma_to_lds<16>(rsrc(p.a + 8 * u * K, left * K), lds_addr(st + St::kW + 8 * u * 128),
-                     ((u & 1) ? off_odd : off_even) + kk);
+                     off_add((u & 1) ? off_odd : off_even, kk));
     }
     uint8_t* sc = st + St::kW + St::kX;
     if constexpr (MODE == MODE_PROMOTE) {
       const int ks = valid ? k * 4 : kOutOfRange;
-      dma_to_lds<4>(rs_sx, lds_addr(sc), lane * nkb * 4 + ks);
-      dma_to_lds<4>(rs_sw, lds_addr(sc + 256), lane * nkb * 4 + ks);
+      dma_to_lds<4>(rs_sx, lds_addr(sc), off_add(lane * nkb * 4, ks));
+      dma_to_lds<4>(rs_sw, lds_addr(sc + 256), off_add(lane * nkb * 4, ks));
     }
     if constexpr (MODE == MODE_MX) {
       const int ks = valid ? k * 4 : kOutOfRange;
-      dma_to_lds<4>(rs_ex, lds_addr(sc), lane * (int)kq + ks);
-      dma_to_lds<4>(rs_ew, lds_addr(sc + 256), lane * (int)kq + ks);
-      dma_to_lds<4>(rs_ew, lds_addr(sc + 512), (64 + lane) * (int)kq + ks);
+      dma_to_lds<4>(rs_ex, lds_addr(sc), off_add(lane * (int)kq, ks));
+      dma_to_lds<4>(rs_ew, lds_addr(sc + 256), off_add(lane * (int)kq, ks));
+      dma_to_lds<4>(rs_ew, lds_addr(sc + 512), off_add((64 + lane) * (int)kq, ks));
     }
     if constexpr (MODE == MODE_MX4) {
       // word wd (UE8M0 bytes 4wd .. 4wd+3 of the step) of X rows at sc + 256 wd,
@@ -134,9 +134,9 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
       const int ks = valid ? k * 8 : kOutOfRange;
 #pragma unroll
       for (int wd = 0; wd < 2; ++wd) {
-        dma_to_lds<4>(rs_ex, lds_addr(sc + 256 * wd), lane * (int)kq + ks + 4 * wd);
-        dma_to_lds<4>(rs_ew, lds_addr(sc + 512 + 512 * wd), lane * (int)kq + ks + 4 * wd);
-        dma_to_lds<4>(rs_ew, lds_addr(sc + 768 + 512 * wd), (64 + lane) * (int)kq + ks + 4 * wd);
+        dma_to_lds<4>(rs_ex, lds_addr(sc + 256 * wd), off_add(lane * (int)kq + 4 * wd, ks));
+        dma_to_lds<4>(rs_ew, lds_addr(sc + 512 + 512 * wd), off_add(lane * (int)kq + 4 * wd, ks));
+        dma_to_lds<4>(rs_ew, lds_addr(sc + 768 + 512 * wd), off_add((64 + lane) * (int)kq + 4 * wd, ks));
       }
     }
     if constexpr (MODE == MODE_NV4 || PAIRS) {
@@ -145,9 +145,9 @@ __device__ __forceinline__ void gemm_skinny_body(const GemmArgs& p, int R) {
       // the offset are multiples of 16): X rows at sc + 16 r, W rows r < 128
       // at sc + 1024 + 16 r
       const int ks = valid ? (PAIRS ? (k & ~1) * 8 : k * 16) : kOutOfRange;
-      dma_to_lds<16>(rs_ex, lds_addr(sc), lane * (int)kq + ks);
-      dma_to_lds<16>(rs_ew, lds_addr(sc + 1024), lane * (int)kq + ks);
-      dma_to_lds<16>(rs_ew, lds_addr(sc + 2048), (64 + lane) * (int)kq + ks);
+      dma_to_lds<16>(rs_ex, lds_addr(sc), off_add(lane * (int)kq, ks));
+      dma_to_lds<16>(rs_ew, lds_addr(sc + 1024), off_add(lane * (int)kq, ks));
+      dma_to_lds<16>(rs_ew, lds_addr(sc + 2048), off_add((64 + lane) * (int)kq, ks));
     }
   };
 
