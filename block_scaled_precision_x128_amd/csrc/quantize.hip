@@ -16,12 +16,16 @@
 //               longer rows take a second pass that re-reads from L2)
 //   BLOCK       one workgroup per 128x128 block, 64 elements per thread
 //   TENSOR      amax partials per workgroup into the workspace, then a second
-//               kernel reduces them and encodes
+//               kernel reduces them and encodes; inputs up to 512 KiB in one
+//               kernel whose every workgroup reduces the whole input itself
 #include "device_common.h"
 #include "given_scale.h"
 #include "kernels.h"
 
 namespace fp8blk {
+
+// Per-tensor inputs up to this size are quantized in one launch (below).
+constexpr int64_t kSmallTensorBytes = 512 * 1024;
 
 // ---- loads of 8 / 32 consecutive elements as fp32 --------------------------
 template <int DT>
@@ -200,6 +204,45 @@ __global__ __launch_bounds__(256) void k_quant_tensor(const void* __restrict__ x
     uint32_t out[2];
     encode_scaled<FMT, 8>(v, s, out);
     *reinterpret_cast<u32x2*>(q + 8 * idx) = u32x2{out[0], out[1]};
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) scales[0] = s;
+}
+
+// Small tensors in one launch: every workgroup reduces the amax of the whole
+// tensor itself (after the first workgroup of an XCD touches the input, its
+// reads hit that XCD's L2) and then encodes its own share of the chunks, so no
+// partial maxima cross workgroups and no second launch waits for them.  The
+// amax is a maximum, so the scale and codes are those of the two-kernel path.
+// 1024 threads with eight 16-byte loads each in flight: the whole-tensor read
+// is bound by the latency of a few rounds of loads, not by bandwidth.
+template <int FMT, int DT>
+__global__ __launch_bounds__(1024) void k_quant_tensor_small(const void* __restrict__ x, uint8_t* __restrict__ q,
+                                                              float* __restrict__ scales, int64_t nch) {
+  __shared__ float red[16];
+  constexpr int T = 1024, U = DT == DT_BF16 ? 8 : 4;   // U chunks (U * 16 bytes) in flight per thread
+  float mu[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) mu[u] = 0.0f;
+  for (int64_t idx = threadIdx.x; idx < nch; idx += U * T) {
+    float v[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (idx + u * T < nch) load8<DT>(x, 8 * (idx + u * T), v[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (idx + u * T < nch) mu[u] = fmaxf(mu[u], local_amax<8>(v[u]));
+  }
+  float m = mu[0];
+#pragma unroll
+  for (int u = 1; u < U; ++u) m = fmaxf(m, mu[u]);
+  m = block_max(m, red);
+  const float s = group_scale<FMT>(m);
+  for (int64_t i = (int64_t)blockIdx.x * T + threadIdx.x; i < nch; i += (int64_t)gridDim.x * T) {
+    float v[8];
+    load8<DT>(x, 8 * i, v);
+    uint32_t out[2];
+    encode_scaled<FMT, 8>(v, s, out);
+    *reinterpret_cast<u32x2*>(q + 8 * i) = u32x2{out[0], out[1]};
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) scales[0] = s;
 }
@@ -384,6 +427,12 @@ static hipError_t quantize_t(const void* x, int64_t rows, int64_t cols, int g, u
         break;
       }
       const int64_t nch = total / 8;
+      if (total * (DT == DT_BF16 ? 2 : 4) <= kSmallTensorBytes) {
+        // one workgroup per 2048 chunks, each reading the whole input once
+        const int64_t gsm = (nch + 2047) / 2048;
+        hipLaunchKernelGGL((k_quant_tensor_small<FMT, DT>), dim3((unsigned)gsm), dim3(1024), 0, st, x, q, s, nch);
+        break;
+      }
       int64_t p = (nch + 1023) / 1024;
       if (p > kTensorPartials) p = kTensorPartials;
       float* partial = reinterpret_cast<float*>(ws);

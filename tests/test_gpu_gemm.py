@@ -164,3 +164,25 @@ def test_gemm_k_zero_writes_zeros():
     fb.fp8_gemm_blockscaled(a, fb.E4M3, T, s, b, fb.E4M3, T, s, fb.DT_F32, out=out)
     torch.cuda.synchronize()
     assert torch.count_nonzero(out).item() == 0
+
+
+@pytest.mark.parametrize("xg,wg", [(R, R), (TL, BL), (MX, MX)])
+def test_gemm_large_tiles_short_k_and_ragged_m(xg, wg):
+    """256x256 tiles (and the 256x192 column split) on one K step, where the
+    step's in-loop loads are all fillers past the descriptors, and on three
+    steps with a ragged last tile row (M = 4000: 160 of its 256 rows valid).
+    Every column of the last tile row, the first rows of every tile row and
+    random rows are checked against the oracle."""
+    for (M, N, K) in [(4096, 4480, 128), (4000, 4480, 384), (4000, 4096, 384)]:
+        xq, sx, wq, sw = _operands(M, N, K, xg, wg, fb.E4M3, fb.E4M3, seed=M + N + K + xg)
+        rng = np.random.default_rng(K + xg)
+        rows = np.unique(np.concatenate([np.arange(3840, M), np.arange(0, M, 256), rng.integers(0, M, 64)]))
+        xr = gemm.dequant_rows(xq[rows], sx, xg, fb.E4M3, rows)
+        wd = gemm.dequant_operand(wq, sw, wg, fb.E4M3)
+        ref, absb = xr @ wd.T, np.abs(xr) @ np.abs(wd).T
+        for accum, rel in ACCUMS:
+            for odt in (fb.DT_F32, fb.DT_BF16):
+                label = f"large tiles pair=({xg},{wg}) {M}x{N}x{K} accum={accum} odt={odt}"
+                say("gemm", label)
+                out = _run(xq, sx, xg, fb.E4M3, wq, sw, wg, fb.E4M3, odt, fb.GEMM_TILED, accum)
+                gemm_check(out[rows], odt, ref, absb, label, rel)
