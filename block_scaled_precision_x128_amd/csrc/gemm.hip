@@ -64,8 +64,10 @@ namespace fp8blk {
 // below), in 128-K steps.  Both operand tiles are FP8 in LDS, in two or three
 // stages; global data goes to LDS with buffer_load ... lds (no register
 // staging), through descriptors that cover only the tile's valid rows, so
-// rows past M or N arrive as zeros.  One barrier per K step: the loads of
-// step k+NS-1 are issued right after it and land while step k computes.
+// rows past M or N arrive as zeros.  One barrier per K step, after which the
+// stage of step k-1 is free: the loads of step k+NS-1 go there, issued a few
+// at a time from inside step k's multiply loop (NVFP4: all at once right
+// after the barrier), and land while later steps compute.
 //
 // LDS tile layout: 128-byte rows of eight 16-byte chunks; chunk c of row r is
 // stored at chunk c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment
@@ -157,7 +159,10 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // 2% faster at c3 and c5 (A/B on one box).
   // So do the exact per-tensor / per-row and MX loops (MX exact 1.4% faster at c5),
   // and the MXFP4 loop (3% faster at 4096x7168x7168); NVFP4 keeps the burst.
-  constexpr bool kRowsInLoop = NS == 2 && MODE != MODE_NV4;
+  // With three stages (128x256 tiles) step kb's loop issues step kb + 2's rows
+  // the same way: native 7.5% faster at 2048x4096x4096 (two A/B runs on one
+  // box, outputs bit-identical), exact 0-2%.
+  constexpr bool kRowsInLoop = MODE != MODE_NV4;
 
   // The TBM A rows and TBN B rows of a K step form one list of LDS rows,
   // 8 rows (1 KiB) per load instruction; wave w issues instructions
@@ -215,6 +220,12 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         dma_to_lds<16>(block_rsrc(is_a ? a_base : b_base, is_a ? rows_a : rows_b, xl),
                        lds_addr(&smem[buf][8 * x * 128]), off_add(goff, kk));
     }
+  };
+  // Row blocks u0 .. u1-1 of step kb + NS - 1, into the stage that step kb's
+  // barrier freed (the stage step kb - 1 read); filler loads past the last step.
+  auto issue_next = [&](int kb, int buf, int u0, int u1) {
+    const int nxt = kb + NS - 1;
+    issue_rows(nxt < nkb ? nxt : -1, buf == 0 ? NS - 1 : buf - 1, u0, u1);
   };
   auto issue_loads = [&](int kb, int buf, bool rows) {
     if (rows) issue_rows(kb, buf, 0, LPW);
@@ -408,7 +419,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       for (int i = 0; i < MI; ++i) {
         if constexpr (kRowsInLoop) {
           if (i & 1)
-            issue_rows(kb + 1 < nkb ? kb + 1 : -1, buf ^ 1, (i >> 1) * LPW / (MI / 2),
+            issue_next(kb, buf, (i >> 1) * LPW / (MI / 2),
                        ((i >> 1) + 1) * LPW / (MI / 2));
         }
         const int r = a_row0 + 16 * i;
@@ -439,7 +450,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       for (int i = 0; i < MI; ++i) {
         if constexpr (kRowsInLoop) {
           if (i & 1)
-            issue_rows(kb + 1 < nkb ? kb + 1 : -1, buf ^ 1, (i >> 1) * LPW / (MI / 2),
+            issue_next(kb, buf, (i >> 1) * LPW / (MI / 2),
                        ((i >> 1) + 1) * LPW / (MI / 2));
         }
         const int r = a_row0 + 16 * i;
@@ -536,7 +547,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
           // step kb + 1's row blocks, spread over the odd N tiles (filler
           // loads on the last step: no branch in the unrolled loop)
           if (j & 1)
-            issue_rows(kb + 1 < nkb ? kb + 1 : -1, buf ^ 1, (j >> 1) * LPW / (NJ / 2),
+            issue_next(kb, buf, (j >> 1) * LPW / (NJ / 2),
                        ((j >> 1) + 1) * LPW / (NJ / 2));
         }
         if (j + 1 < NJ) {
@@ -613,7 +624,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
             // issues filler loads: no branch inside the unrolled loop, which
             // measured to cost register spills)
             if (i & 1)
-              issue_rows(kb + 1 < nkb ? kb + 1 : -1, buf ^ 1, (i >> 1) * LPW / (MI / 2),
+              issue_next(kb, buf, (i >> 1) * LPW / (MI / 2),
                          ((i >> 1) + 1) * LPW / (MI / 2));
           }
           if (i + 1 < MI) {
@@ -664,7 +675,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         for (int i = 0; i < MI; ++i) {
           if constexpr (kRowsInLoop) {
             if (i & 1)
-              issue_rows(kb + 1 < nkb ? kb + 1 : -1, buf ^ 1, (i >> 1) * LPW / (MI / 2),
+              issue_next(kb, buf, (i >> 1) * LPW / (MI / 2),
                          ((i >> 1) + 1) * LPW / (MI / 2));
           }
           const int r = a_row0 + 16 * i;
@@ -700,7 +711,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       // the main loop issues a step's row blocks from inside its multiply
       // loop; here (including the step the main loop left) they go out whole
       if constexpr (kRowsInLoop) {
-        if (kb + 1 < nkb) issue_rows(kb + 1, buf ^ 1, 0, LPW);
+        if (kb + NS - 1 < nkb) issue_next(kb, buf, 0, LPW);
       }
       const uint8_t* sa_ = &smem[buf][0];
       const uint8_t* sb_ = &smem[buf][TBM * TBK];
