@@ -158,11 +158,12 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // The FP8 native loop (every scale mode) issues its loads the same way:
   // 2% faster at c3 and c5 (A/B on one box).
   // So do the exact per-tensor / per-row and MX loops (MX exact 1.4% faster at c5),
-  // and the MXFP4 loop (3% faster at 4096x7168x7168); NVFP4 keeps the burst.
+  // the MXFP4 loop (3% faster at 4096x7168x7168) and, once the loads went out
+  // over the first half of the loop (below), the NVFP4 loop (1.6%).
   // With three stages (128x256 tiles) step kb's loop issues step kb + 2's rows
   // the same way: native 7.5% faster at 2048x4096x4096 (two A/B runs on one
   // box, outputs bit-identical), exact 0-2%.
-  constexpr bool kRowsInLoop = MODE != MODE_NV4;
+  constexpr bool kRowsInLoop = true;
 
   // The TBM A rows and TBN B rows of a K step form one list of LDS rows,
   // 8 rows (1 KiB) per load instruction; wave w issues instructions
@@ -513,6 +514,9 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         for (int j = 0; j < NJ; ++j) frag(sb_, b_row0 + 16 * j, TBM + b_row0 + 16 * j, h, xb[j]);
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
+          if constexpr (kRowsInLoop) {
+            if (h == 0) issue_part(kb, buf, i, MI / 2);
+          }
           Op xa[4];
           frag(sa_, a_row0 + 16 * i, a_row0 + 16 * i, h, xa);
 #pragma unroll
