@@ -148,22 +148,18 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   const int64_t rows_a = (M - m0) < TBM ? (M - m0) : TBM;
   const int64_t rows_b = (N - n0) < TBN ? (N - n0) : TBN;
 
-  // Two-stage exact promotion: the row-block loads of step kb + 1 are issued
-  // from inside step kb's multiply loop, a few at a time, rather than all at
-  // once after the barrier.  A burst of load instructions there stalls the
-  // waves that issue it while both waves of every SIMD are converting their
-  // B operands, and the matrix cores idle; spread through the loop the loads
-  // overlap the other wave's multiplies (256x256 tiles at 4096x7168x7168: 6%
-  // faster; the 256x192 tiles, more VALU-bound, gain nothing).
-  // The FP8 native loop (every scale mode) issues its loads the same way:
-  // 2% faster at c3 and c5 (A/B on one box).
-  // So do the exact per-tensor / per-row and MX loops (MX exact 1.4% faster at c5),
-  // the MXFP4 loop (3% faster at 4096x7168x7168) and, once the loads went out
-  // over the first half of the loop (below), the NVFP4 loop (1.6%).
-  // With three stages (128x256 tiles) step kb's loop issues step kb + 2's rows
-  // the same way: native 7.5% faster at 2048x4096x4096 (two A/B runs on one
-  // box, outputs bit-identical), exact 0-2%.
-  constexpr bool kRowsInLoop = true;
+  // The row-block loads of step kb + NS - 1 are issued from inside step kb's
+  // multiply loop, a few at a time, rather than all at once after the
+  // barrier.  A burst of load instructions there stalls the waves that issue
+  // it while both waves of every SIMD are converting their B operands, and the
+  // matrix cores idle; inside the loop the loads overlap the other wave's
+  // multiplies.  Measured against the burst (A/B on one box, outputs
+  // bit-identical): exact promotion 256x256 tiles at 4096x7168x7168 6% faster
+  // (the 256x192 tiles, more VALU-bound, gained nothing), the FP8 native loop
+  // 2% at c3 and c5, the exact MX loop 1.4% at c5, the MXFP4 loop 3%, and with
+  // three stages (128x256 tiles) the native loop 7.5% at 2048x4096x4096 (exact
+  // 0-2%); then, issued over the first half of the loop (issue_part below),
+  // the NVFP4 loop 1.6%.
 
   // The TBM A rows and TBN B rows of a K step form one list of LDS rows,
   // 8 rows (1 KiB) per load instruction; wave w issues instructions
@@ -171,19 +167,15 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // which holds logical chunk (q%8) ^ lds_swz(row).
   // Row 8x + q/8 has lds_swz = (q/8) ^ (x & 1), so a lane's offset inside its
   // 8-row block is one of two per-lane values.  Descriptors cover only the
-  // tile's valid rows (rows past M or N read zeros).  The block is selected
-  // either by a descriptor that starts at its first row (scalar arithmetic
-  // only; the loads issued all at once after the barrier), or, where the
-  // loads are issued from inside the multiply loop, by a wave-uniform offset
-  // added to the lane's offset in one descriptor per operand (one descriptor
-  // per block kept live through the loop costs scalar registers there).
-  // Offsets stay below 256 * K <= 2^30 bytes.
+  // tile's valid rows (rows past M or N read zeros).  The block is selected by
+  // a wave-uniform offset added to the lane's offset inside the load's
+  // assembly, in one descriptor per operand (a descriptor per block, kept live
+  // through the multiply loop, costs scalar registers; offsets precomputed by
+  // the compiler cost a vector register per load).  Offsets stay below
+  // 256 * K <= 2^30 bytes.
   const int q8 = lane >> 3;
   const int goff_even = q8 * (int)KB + (((lane & 7) ^ q8) << 4);
   const int goff_odd = q8 * (int)KB + (((lane & 7) ^ q8 ^ 1) << 4);
-  auto block_rsrc = [&](const uint8_t* base, int64_t rows, int x) {  // x: 8-row block inside its tile
-    return uniform_rsrc(base + 8 * x * KB, (rows - 8 * x) * KB);
-  };
   const uint8_t* a_base = p.a + m0 * KB;
   const uint8_t* b_base = p.b + n0 * KB;
   const __amdgpu_buffer_rsrc_t rs_a = uniform_rsrc(a_base, rows_a * KB), rs_b = uniform_rsrc(b_base, rows_b * KB);
@@ -214,12 +206,8 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       const bool is_a = 8 * x < TBM;   // wave-uniform: scalar selects, no branch
       const int xl = is_a ? x : x - TBM / 8;
       const int goff = (x & 1) ? goff_odd : goff_even;
-      if constexpr (kRowsInLoop)
-        dma16_to_lds_add(is_a ? rs_a : rs_b, lds_addr(&smem[buf][8 * x * 128]), goff,
-                         __builtin_amdgcn_readfirstlane(off_add(xl * 8 * (int)KB, kk)));
-      else
-        dma_to_lds<16>(block_rsrc(is_a ? a_base : b_base, is_a ? rows_a : rows_b, xl),
-                       lds_addr(&smem[buf][8 * x * 128]), off_add(goff, kk));
+      dma16_to_lds_add(is_a ? rs_a : rs_b, lds_addr(&smem[buf][8 * x * 128]), goff,
+                       __builtin_amdgcn_readfirstlane(off_add(xl * 8 * (int)KB, kk)));
     }
   };
   // Row blocks u0 .. u1-1 of step kb + NS - 1, into the stage that step kb's
@@ -358,7 +346,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
-    if (kb + NS - 1 < nkb) issue_loads(kb + NS - 1, buf == 0 ? NS - 1 : buf - 1, !kRowsInLoop);
+    if (kb + NS - 1 < nkb) issue_loads(kb + NS - 1, buf == 0 ? NS - 1 : buf - 1, false);
   };
 
   int buf = 0;   // stage of step kb
@@ -428,9 +416,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       }
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        if constexpr (kRowsInLoop) {
-          issue_part(kb, buf, i, MI / 2);
-        }
+        issue_part(kb, buf, i, MI / 2);
         const int r = a_row0 + 16 * i;
         const u32x4 al = lds16(sa_, r * 128 + c0), ah = lds16(sa_, r * 128 + c1);
         const uint2 e = scale_words(r);
@@ -457,9 +443,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       if constexpr (kPrefetchA) fa_next = join(lds16(sa_, a_row0 * 128 + c0), lds16(sa_, a_row0 * 128 + c1));
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        if constexpr (kRowsInLoop) {
-          issue_part(kb, buf, i, MI / 2);
-        }
+        issue_part(kb, buf, i, MI / 2);
         const int r = a_row0 + 16 * i;
         v8i fa;
         if constexpr (kPrefetchA) {
@@ -514,9 +498,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         for (int j = 0; j < NJ; ++j) frag(sb_, b_row0 + 16 * j, TBM + b_row0 + 16 * j, h, xb[j]);
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-          if constexpr (kRowsInLoop) {
-            if (h == 0) issue_part(kb, buf, i, MI / 2);
-          }
+          if (h == 0) issue_part(kb, buf, i, MI / 2);
           Op xa[4];
           frag(sa_, a_row0 + 16 * i, a_row0 + 16 * i, h, xa);
 #pragma unroll
@@ -553,11 +535,9 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       xbv[3] = cvt8<BF>(n1.z, n1.w, 1.0f);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        if constexpr (kRowsInLoop) {
-          // the next step's row blocks over the first half of the N tiles
-          // (filler loads on the last step: no branch in the unrolled loop)
-          issue_part(kb, buf, j, NJ / 2);
-        }
+        // the next step's row blocks over the first half of the N tiles
+        // (filler loads on the last step: no branch in the unrolled loop)
+        issue_part(kb, buf, j, NJ / 2);
         if (j + 1 < NJ) {
           const int r = b_row0 + 16 * (j + 1);
           n0 = lds16(sb_, r * 128 + c0);
@@ -627,12 +607,10 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         xa[3] = cvt8<AF>(n1.z, n1.w, 1.0f);
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-          if constexpr (kRowsInLoop) {
-            // the next step's row blocks over the first half of the A tiles
-            // (the last step issues filler loads: no branch inside the
-            // unrolled loop, which measured to cost register spills)
-            issue_part(kb, buf, i, MI / 2);
-          }
+          // the next step's row blocks over the first half of the A tiles
+          // (the last step issues filler loads: no branch inside the
+          // unrolled loop, which measured to cost register spills)
+          issue_part(kb, buf, i, MI / 2);
           if (i + 1 < MI) {
             const int r = a_row0 + 16 * (i + 1);
             n0 = lds16(sa_, r * 128 + c0);
@@ -679,9 +657,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       } else {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
-          if constexpr (kRowsInLoop) {
-            issue_part(kb, buf, i, MI / 2);
-          }
+          issue_part(kb, buf, i, MI / 2);
           const int r = a_row0 + 16 * i;
           const float fsa = (MODE == MODE_MX) ? e8m0_to_f32((s_e[buf][0][r] >> (8 * g)) & 0xffu) : 1.0f;
           const u32x4 d0 = lds16(sa_, r * 128 + c0), d1 = lds16(sa_, r * 128 + c1);
@@ -701,7 +677,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   }
   // the last step's filler loads still write LDS: drain them before the
   // workgroup can exit
-  if constexpr (kRowsInLoop) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if constexpr (MX_WORDS) {
     // Block-by-block exact MX: one 32-K block b of the step per instruction,
@@ -714,9 +690,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       if (!first) sync_step(kb, buf);
       // the main loop issues a step's row blocks from inside its multiply
       // loop; here (including the step the main loop left) they go out whole
-      if constexpr (kRowsInLoop) {
-        if (kb + NS - 1 < nkb) issue_next(kb, buf, 0, LPW);
-      }
+      if (kb + NS - 1 < nkb) issue_next(kb, buf, 0, LPW);
       const uint8_t* sa_ = &smem[buf][0];
       const uint8_t* sb_ = &smem[buf][TBM * TBK];
 #pragma unroll 1
