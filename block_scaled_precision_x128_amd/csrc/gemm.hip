@@ -224,7 +224,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // one (A/B on one box, outputs bit-identical); over the first quarter, or
   // all at the first tile, was slower than the first half.
   auto issue_part = [&](int kb, int buf, int t, int P) {
-    if (t < P) issue_next(kb, buf, t * LPW / P, (t + 1) * LPW / P);
+    if (t >= 0 && t < P) issue_next(kb, buf, t * LPW / P, (t + 1) * LPW / P);
   };
   auto issue_loads = [&](int kb, int buf, bool rows) {
     if (rows) issue_rows(kb, buf, 0, LPW);
@@ -439,11 +439,14 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       // Outside promotion the next A fragment is read one tile ahead (MX: 2.6%
       // faster at c5; with promotion it measured 2.7% slower at c3).
       constexpr bool kPrefetchA = MODE != MODE_PROMOTE;
+      constexpr int kIssueFrom = MODE == MODE_PROMOTE ? 1 : 0;
       v8i fa_next = {};
       if constexpr (kPrefetchA) fa_next = join(lds16(sa_, a_row0 * 128 + c0), lds16(sa_, a_row0 * 128 + c1));
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        issue_part(kb, buf, i, MI / 2);
+        // with promotion the loads go out from the second tile on: 2-3% faster
+        // at c3 (two A/B runs on one box); the MX loop lost 2% that way
+        if (i >= kIssueFrom) issue_part(kb, buf, i - kIssueFrom, MI / 2);
         const int r = a_row0 + 16 * i;
         v8i fa;
         if constexpr (kPrefetchA) {
