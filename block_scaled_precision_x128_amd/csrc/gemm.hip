@@ -156,10 +156,10 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // multiplies.  Measured against the burst (A/B on one box, outputs
   // bit-identical): exact promotion 256x256 tiles at 4096x7168x7168 6% faster
   // (the 256x192 tiles, more VALU-bound, gained nothing), the FP8 native loop
-  // 2% at c3 and c5, the exact MX loop 1.4% at c5, the MXFP4 loop 3%, and with
-  // three stages (128x256 tiles) the native loop 7.5% at 2048x4096x4096 (exact
-  // 0-2%); then, issued over the first half of the loop (issue_part below),
-  // the NVFP4 loop 1.6%.
+  // 2% at 4096x7168x7168 and 8192^3, the exact MX loop 1.4% at 8192^3, the
+  // MXFP4 loop 3%, and with three stages (128x256 tiles) the native loop 7.5%
+  // at 2048x4096x4096 (exact 0-2%); then, issued over the first half of the
+  // loop (issue_part below), the NVFP4 loop 1.6%.
 
   // The TBM A rows and TBN B rows of a K step form one list of LDS rows,
   // 8 rows (1 KiB) per load instruction; wave w issues instructions
@@ -220,9 +220,9 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // (LPW / P) of those row blocks, so they are all in flight by the middle of
   // the step.  Spread over the whole loop (odd tiles), the last ones went out
   // too late to land before the next step's wait: issuing them over the first
-  // half measured 4% faster on the exact path (c3 and c5) and 6% on the native
-  // one (A/B on one box, outputs bit-identical); over the first quarter, or
-  // all at the first tile, was slower than the first half.
+  // half measured 4% faster on the exact path (4096x7168x7168 and 8192^3) and
+  // 6% on the native one (A/B on one box, outputs bit-identical); over the
+  // first quarter, or all at the first tile, was slower than the first half.
   auto issue_part = [&](int kb, int buf, int t, int P) {
     if (t >= 0 && t < P) issue_next(kb, buf, t * LPW / P, (t + 1) * LPW / P);
   };
@@ -437,7 +437,8 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         if constexpr (MODE == MODE_MX) eb[j] = (int)((s_e[buf][0][TBM + r] >> (8 * g)) & 0xffu);
       }
       // Outside promotion the next A fragment is read one tile ahead (MX: 2.6%
-      // faster at c5; with promotion it measured 2.7% slower at c3).
+      // faster at 8192^3; with promotion it measured 2.7% slower at
+      // 4096x7168x7168).
       constexpr bool kPrefetchA = MODE != MODE_PROMOTE;
       constexpr int kIssueFrom = MODE == MODE_PROMOTE ? 1 : 0;
       v8i fa_next = {};
@@ -445,7 +446,8 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         // with promotion the loads go out from the second tile on: 2-3% faster
-        // at c3 (two A/B runs on one box); the MX loop lost 2% that way
+        // at 4096x7168x7168 (two A/B runs on one box); the MX loop lost 2%
+        // that way
         if (i >= kIssueFrom) issue_part(kb, buf, i - kIssueFrom, MI / 2);
         const int r = a_row0 + 16 * i;
         v8i fa;
