@@ -850,6 +850,13 @@ template <int AF, int BF, int MODE, int ODT, int PATH>
 __global__ __launch_bounds__(512, 1) void k_gemm_tiled_128x256(GemmArgs p) {
   gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 4, 4, MODE == MODE_NV4 ? 2 : 3>(p);
 }
+// 64x64 tiles of 4 waves (32x32 wave tiles, three stages) for problems so
+// small that 128x256 tiles would leave almost every CU idle (128x256x512: one
+// tile, whose 128 KiB fp32 result one CU alone would store).
+template <int AF, int BF, int MODE, int ODT, int PATH>
+__global__ __launch_bounds__(256, 1) void k_gemm_tiled_64x64(GemmArgs p) {
+  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 2, 2, 2, 3>(p);
+}
 
 
 // ---------------------------------------------------------------------------
@@ -898,6 +905,16 @@ static void tiled_shape(const GemmArgs& p, hipStream_t st) {
   const int64_t big_tiles = ntm * ((p.N + 255) / 256);
   if (big_tiles < cus) {
     const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 255) / 256);
+    // (Not for the exact MX path: its switch to block-by-block sums is taken
+    // per wave, over the wave's rows, so 32-row waves would round some sums
+    // differently from the 64-row waves the quantized-output GEMM uses.)
+    if constexpr (ODT < ODT_Q_E4M3 && MODE <= MODE_MX && !(MODE == MODE_MX && PATH == PATH_EXACT)) {
+      if (tiles * 8 <= cus) {
+        const int64_t small = ((p.M + 63) / 64) * ((p.N + 63) / 64);
+        hipLaunchKernelGGL((k_gemm_tiled_64x64<AF, BF, MODE, ODT, PATH>), dim3((unsigned)small), dim3(256), 0, st, p);
+        return;
+      }
+    }
     hipLaunchKernelGGL((k_gemm_tiled_128x256<AF, BF, MODE, ODT, PATH>), dim3((unsigned)tiles), dim3(512), 0, st, p);
     return;
   }

@@ -7,7 +7,7 @@
   are ordinary fp32 numbers even though one operand's scale is 2^-127 .. 2^-124
   and the other's 2^124 .. 2^127, so the 1e-4 * sum|x w| bound applies.  Codes
   cover every finite code of the format.  Both kernels (tiled, skinny), every
-  tiled tile shape (128x256, 256x256, the 256x192 column split) and both
+  tiled tile shape (64x64, 128x256, 256x256, the 256x192 column split) and both
   orientations; steps switching from foldable to unfoldable exponents midway.
 * Operands the quantizer itself makes at those ends: blocks with amax near the
   fp32 maximum (e = 120 for E4M3, codes whose value exceeds fp32's range on its
@@ -65,7 +65,8 @@ def _check(xq, sx, xf, wq, sw, wf, algo, accum, label, rows=None):
 
 
 SHAPES = [(16, 256, 1024, fb.GEMM_SKINNY),     # skinny kernel
-          (128, 256, 1024, fb.GEMM_TILED),     # 128x256 tiles, three stages
+          (128, 256, 1024, fb.GEMM_TILED),     # 64x64 tiles (tiny problem)
+          (1024, 2048, 1024, fb.GEMM_TILED),   # 128x256 tiles, three stages
           (4096, 4096, 256, fb.GEMM_TILED),    # 256x256 tiles
           (4096, 4480, 256, fb.GEMM_TILED),    # 256x256 + the 256x192 column split
           (4096, 4096, 1024, fb.GEMM_TILED)]   # 256x256 tiles leaving the main loop at step 2 of 8
