@@ -850,9 +850,13 @@ template <int AF, int BF, int MODE, int ODT, int PATH>
 __global__ __launch_bounds__(512, 1) void k_gemm_tiled_128x256(GemmArgs p) {
   gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 4, 4, MODE == MODE_NV4 ? 2 : 3>(p);
 }
-// 64x64 tiles of 4 waves (32x32 wave tiles, three stages) for problems so
-// small that 128x256 tiles would leave almost every CU idle (128x256x512: one
-// tile, whose 128 KiB fp32 result one CU alone would store).
+// 64x64 tiles of 4 waves (32x32 wave tiles, three stages) for problems whose
+// 128x256 tiles would leave many CUs idle (128x256x512: one tile, whose
+// 128 KiB fp32 result one CU alone would store).  Their conversions per MFMA
+// double, so they pay only below a share of the CUs: measured (A/B on one
+// box) exact 106 -> 51 us at 256x7168x7168 (56 tiles of 128x256), 64 -> 53 us
+// at 1024x4096x4096 (128 tiles); native 67 -> 43 us at 56 tiles but 37 -> 39
+// us at 128.
 template <int AF, int BF, int MODE, int ODT, int PATH>
 __global__ __launch_bounds__(256, 1) void k_gemm_tiled_64x64(GemmArgs p) {
   gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 2, 2, 2, 3>(p);
@@ -909,7 +913,7 @@ static void tiled_shape(const GemmArgs& p, hipStream_t st) {
     // per wave, over the wave's rows, so 32-row waves would round some sums
     // differently from the 64-row waves the quantized-output GEMM uses.)
     if constexpr (ODT < ODT_Q_E4M3 && MODE <= MODE_MX && !(MODE == MODE_MX && PATH == PATH_EXACT)) {
-      if (tiles * 8 <= cus) {
+      if (PATH == PATH_EXACT ? 5 * tiles <= 3 * cus : 4 * tiles <= cus) {
         const int64_t small = ((p.M + 63) / 64) * ((p.N + 63) / 64);
         hipLaunchKernelGGL((k_gemm_tiled_64x64<AF, BF, MODE, ODT, PATH>), dim3((unsigned)small), dim3(256), 0, st, p);
         return;

@@ -170,10 +170,12 @@ def test_gemm_k_zero_writes_zeros():
 def test_gemm_large_tiles_short_k_and_ragged_m(xg, wg):
     """256x256 tiles (and the 256x192 column split) on one K step, where the
     step's in-loop loads are all fillers past the descriptors, and on three
-    steps with a ragged last tile row (M = 4000: 160 of its 256 rows valid).
-    Every column of the last tile row, the first rows of every tile row and
-    random rows are checked against the oracle."""
-    for (M, N, K) in [(4096, 4480, 128), (4000, 4480, 384), (4000, 4096, 384)]:
+    steps with a ragged last tile row (M = 4000: 160 of its 256 rows valid);
+    and 128x256 tiles on every path at 2560x2048 (160 tiles, too many for the
+    64x64 tiles of smaller problems).  Every column of the last tile row, the
+    first rows of every tile row and random rows are checked against the
+    oracle."""
+    for (M, N, K) in [(4096, 4480, 128), (4000, 4480, 384), (4000, 4096, 384), (2560, 2048, 640)]:
         xq, sx, wq, sw = _operands(M, N, K, xg, wg, fb.E4M3, fb.E4M3, seed=M + N + K + xg)
         rng = np.random.default_rng(K + xg)
         rows = np.unique(np.concatenate([np.arange(3840, M), np.arange(0, M, 256), rng.integers(0, M, 64)]))

@@ -66,7 +66,7 @@ def _check(xq, sx, xf, wq, sw, wf, algo, accum, label, rows=None):
 
 SHAPES = [(16, 256, 1024, fb.GEMM_SKINNY),     # skinny kernel
           (128, 256, 1024, fb.GEMM_TILED),     # 64x64 tiles (tiny problem)
-          (1024, 2048, 1024, fb.GEMM_TILED),   # 128x256 tiles, three stages
+          (2048, 2048, 1024, fb.GEMM_TILED),   # 128x256 tiles, three stages
           (4096, 4096, 256, fb.GEMM_TILED),    # 256x256 tiles
           (4096, 4480, 256, fb.GEMM_TILED),    # 256x256 + the 256x192 column split
           (4096, 4096, 1024, fb.GEMM_TILED)]   # 256x256 tiles leaving the main loop at step 2 of 8
