@@ -66,8 +66,8 @@ namespace fp8blk {
 // staging), through descriptors that cover only the tile's valid rows, so
 // rows past M or N arrive as zeros.  One barrier per K step, after which the
 // stage of step k-1 is free: the loads of step k+NS-1 go there, issued a few
-// at a time from inside step k's multiply loop (NVFP4: all at once right
-// after the barrier), and land while later steps compute.
+// at a time from the first half of step k's multiply loop, and land while
+// later steps compute.
 //
 // LDS tile layout: 128-byte rows of eight 16-byte chunks; chunk c of row r is
 // stored at chunk c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1).  A fragment
