@@ -828,11 +828,12 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   }
 }
 
-// Kernels for the workgroup shapes, all with 8 waves: 256x256 and 256x192
-// (wave tiles 128x64 and 128x48, two LDS stages), and 128x256 (wave tiles
+// Kernels for the workgroup shapes, 8 waves each: 256x256 and 256x192 (wave
+// tiles 128x64, and 64x96 or 128x48, two LDS stages), and 128x256 (wave tiles
 // 64x64, three LDS stages) for problems with fewer 256x256 tiles than CUs,
 // where the deeper pipeline measured 13% faster and the smaller tile's lower
-// arithmetic intensity does not matter.
+// arithmetic intensity does not matter; and 64x64 with 4 waves for small
+// problems (below).
 template <int AF, int BF, int MODE, int ODT, int PATH>
 __global__ __launch_bounds__(512, 1) void k_gemm_tiled_256x256(GemmArgs p) {
   gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 8, 4, 2>(p);
