@@ -309,7 +309,6 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // (the only layout that takes the transposed products).
   constexpr bool kStreamB = kTransposed && NJ > MI;
   static_assert(!kTransposed || kStreamB, "transposed products are formed by the streamed-B loop only");
-  static_assert(!kTransposed || ODT < ODT_Q_E4M3, "the quantized epilogue takes the untransposed layout");
   int jblk[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -730,11 +729,79 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   }
 
   // epilogue
-  if constexpr (ODT == ODT_Q_E4M3 || ODT == ODT_Q_E5M2) {
-    // The result quantized to FP8 for the next layer, exactly as the
-    // quantizer does it to the fp32 values the DT_F32 output would hold:
-    // per row and 128 columns, amax -> s = RN(amax / Vmax) -> sat_rne(RN(v / s)).
-    // A 128-column group is the tiles of two neighbouring waves (wn, wn ^ 1).
+  // The quantized outputs: the result quantized to FP8 for the next layer,
+  // exactly as the quantizer does it to the fp32 values the DT_F32 output
+  // would hold: per row and 128 columns, amax -> s = RN(amax / Vmax) ->
+  // sat_rne(RN(v / s)).  Tile scales are stored with a row stride of ldo / 128
+  // (the whole output's groups per row), so a column range of the output can
+  // be computed as a problem of its own.
+  if constexpr ((ODT == ODT_Q_E4M3 || ODT == ODT_Q_E5M2) && kTransposed) {
+    // Transposed products: lane l holds row 16 i + l%16, columns 16 j + 4 g + q.
+    // The tile starts on a 128-column group; a wave's WC < 128 columns meet at
+    // most two groups (slots 0, 1), and a 16-column tile lies in one.  Each
+    // wave takes |v| per row over its columns of each group, the waves that
+    // share a group combine those partial maxima through LDS, and each lane
+    // encodes its four consecutive values of an N tile under their group's
+    // scale, one 4-byte store.
+    constexpr int QF = ODT == ODT_Q_E4M3 ? FMT_E4M3 : FMT_E5M2;
+    static_assert(TBN % 128 == 0 && WC < 128, "tiles on group boundaries, waves narrower than a group");
+    constexpr int kSpan = 128 / WC + 1;   // most waves that share a group
+    __shared__ float s_pmax[NW][2][WR];
+    const int cw = wn * WC, tg0 = cw >> 7;   // the wave's first tile column and its group
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      float pm[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        float m = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) m = fmaxf(m, fabsf(acc[i][j][q]));
+        if (((cw + 16 * j) >> 7) == tg0) pm[0] = fmaxf(pm[0], m);
+        else pm[1] = fmaxf(pm[1], m);
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        pm[s] = fmaxf(pm[s], __shfl_xor(pm[s], 16));   // over the 4 lanes that hold this row
+        pm[s] = fmaxf(pm[s], __shfl_xor(pm[s], 32));
+        if (g == 0) s_pmax[w][s][16 * i + (lane & 15)] = pm[s];
+      }
+    }
+    __syncthreads();
+    const int64_t nsg = N / 128, srow = p.ldo / 128;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int rl = 16 * i + (lane & 15);   // row within the wave tile
+      const int64_t row = m0 + wm * WR + rl;
+      float sc[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int tg = tg0 + s;   // a tile group past the tile (slot 1 unused) reads no wave
+        const int lo = (tg * 128) / WC, hi = (tg * 128 + 127) / WC < WNW - 1 ? (tg * 128 + 127) / WC : WNW - 1;
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kSpan; ++k) {
+          const int wn2 = lo + k;
+          if (wn2 <= hi) amax = fmaxf(amax, s_pmax[wm * WNW + wn2][tg - ((wn2 * WC) >> 7)][rl]);
+        }
+        sc[s] = group_scale<QF>(amax);
+      }
+      if (row >= M) continue;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int cl = cw + 16 * j;   // the N tile's first tile column
+        const int64_t grp = (n0 + cl) / 128;
+        if (grp >= nsg) continue;     // (N % 128 == 0: a group is stored whole or not at all)
+        const float s = ((cl >> 7) == tg0) ? sc[0] : sc[1];
+        const float v4[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+        uint32_t codes;
+        encode_scaled<QF, 4>(v4, s, &codes);
+        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(p.out) + row * p.ldo + n0 + cl + 4 * g) = codes;
+        if (((cl + 4 * g) & 127) == 0) p.out_scales[row * srow + grp] = s;
+      }
+    }
+  } else if constexpr (ODT == ODT_Q_E4M3 || ODT == ODT_Q_E5M2) {
+    // Untransposed (lane l holds rows 16 i + 4 g + q, column 16 j + l%16): a
+    // 128-column group is the tiles of two neighbouring waves (wn, wn ^ 1).
     constexpr int QF = ODT == ODT_Q_E4M3 ? FMT_E4M3 : FMT_E5M2;
     static_assert(WC == 64 && WNW % 2 == 0, "a 128-column group must be two 64-column wave tiles");
     __shared__ float s_amax[NW][WR];
@@ -766,8 +833,8 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
         if ((lane & 15) == 0) s_amax[w][16 * i + 4 * g + q] = rmax[i][q];
       }
     __syncthreads();
-    const int64_t nsg = N / 128;                     // scale groups per row
-    const int64_t grp = (n0 + wn * WC) / 128;        // this wave's group
+    const int64_t nsg = N / 128, srow = p.ldo / 128;   // scale groups per row, row stride of the scales
+    const int64_t grp = (n0 + wn * WC) / 128;          // this wave's group
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int64_t rbase = m0 + wm * WR + i * 16;
@@ -784,7 +851,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
           uint8_t* o = static_cast<uint8_t*>(p.out) + row * p.ldo + n0 + wn * WC + (lane & 15);
 #pragma unroll
           for (int j = 0; j < NJ; ++j) o[16 * j] = (uint8_t)(codes >> (8 * j));
-          if ((wn & 1) == 0 && (lane & 15) == 0) p.out_scales[row * nsg + grp] = s;
+          if ((wn & 1) == 0 && (lane & 15) == 0) p.out_scales[row * srow + grp] = s;
         }
       }
     }
@@ -851,6 +918,14 @@ template <int AF, int BF, int MODE, int ODT, int PATH>
 __global__ __launch_bounds__(512, 1) void k_gemm_tiled_128x256(GemmArgs p) {
   gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 4, 4, MODE == MODE_NV4 ? 2 : 3>(p);
 }
+// 128x384 tiles (wave tiles 64x96, transposed products, two stages): the
+// last wave of tiles of an exact-promotion GEMM with quantized output, whose
+// 128-column scale groups must not straddle tiles as the 256x192 tiles'
+// would; three quarters of a 256x256 tile's work, like those.
+template <int AF, int BF, int MODE, int ODT, int PATH>
+__global__ __launch_bounds__(512, 1) void k_gemm_tiled_128x384(GemmArgs p) {
+  gemm_tiled_body<AF, BF, MODE, ODT, PATH, 2, 4, 4, 6, 2>(p);
+}
 // 64x64 tiles of 4 waves (32x32 wave tiles, three stages) for problems whose
 // 128x256 tiles would leave many CUs idle (128x256x512: one tile, whose
 // 128 KiB fp32 result one CU alone would store).  Their conversions per MFMA
@@ -886,7 +961,8 @@ hipError_t launch_fill_f32(float* out, int64_t n, float v, hipStream_t st) {
 
 // ---- dispatch over formats, modes, output dtype, path and tile shape ---------
 // Tile shapes: 256x256 when that gives at least one tile per CU (with a
-// 256x192 remainder, below), else 128x256.
+// 256x192 remainder, or 128x384 for the quantized outputs, below), else
+// 128x256 or 64x64.
 
 // The columns [c0, c0 + n) of the problem as a problem of its own (c0 is a
 // multiple of 128, so every scale layout splits at a block boundary).
@@ -895,7 +971,8 @@ static GemmArgs column_range(const GemmArgs& p, int64_t c0, int64_t n, int mode,
   const bool fp4 = mode == MODE_MX4 || mode == MODE_MX4_PAIRS || mode == MODE_NV4;
   q.b = p.b + c0 * (fp4 ? p.K / 2 : p.K);
   q.N = n;
-  q.out = static_cast<uint8_t*>(p.out) + c0 * (odt == DT_F32 ? 4 : 2);
+  q.out = static_cast<uint8_t*>(p.out) + c0 * (odt == DT_F32 ? 4 : (odt == DT_BF16 ? 2 : 1));
+  if (odt == ODT_Q_E4M3 || odt == ODT_Q_E5M2) q.out_scales = p.out_scales + c0 / 128;
   if (mode == MODE_PROMOTE) q.sb = static_cast<const float*>(p.sb) + (c0 / 128) * (p.K / 128);
   else if (mode == MODE_MX || mode == MODE_MX4 || mode == MODE_MX4_PAIRS) q.sb = static_cast<const uint8_t*>(p.sb) + c0 * (p.K / 32);
   else if (mode == MODE_NV4) q.sb = static_cast<const uint8_t*>(p.sb) + c0 * (p.K / 16);
@@ -929,7 +1006,10 @@ static void tiled_shape(const GemmArgs& p, hipStream_t st) {
   // one wave of 256x192 tiles (three quarters of the work per tile), launched
   // right after: e.g. 4096x7168 runs as 256 + 256 tiles in 1.75 tile-times
   // instead of 448 tiles in 2.
-  // (The quantized outputs need 64-column wave tiles: no split for them.)
+  // The quantized outputs cannot take 256x192 tiles, whose 128-column scale
+  // groups would straddle two tiles: exact promotion does its last wave in
+  // 128x384 tiles instead (4096x7168x7168: 256 + 256 tiles), other modes do
+  // not split.
   // The exact path splits: its steps are bound by the VALU and matrix work,
   // which shrinks with the tile.  The FP8 native path is bound per step by
   // load and LDS latency, so a 256x192 tile takes about as long as a 256x256
@@ -937,17 +1017,23 @@ static void tiled_shape(const GemmArgs& p, hipStream_t st) {
   // tiles was 7-8% faster than the split there.  MXFP4 with step-pair scale
   // staging splits too: 2% faster, A/B on one box (MXFP4 with word-by-word
   // staging measured equal either way).
-  if ((PATH == PATH_EXACT || MODE == MODE_MX4_PAIRS) && ODT < ODT_Q_E4M3 && big_tiles % cus != 0 &&
-      cus % ntm == 0) {
-    const int64_t wave_cols = (cus / ntm) * 256;
-    const int64_t n1 = (p.N / wave_cols) * wave_cols, n2 = p.N - n1;
-    if (n1 > 0 && n2 > 0 && ntm * ((n2 + 191) / 192) <= cus) {
+  constexpr bool kQuantOut = ODT == ODT_Q_E4M3 || ODT == ODT_Q_E5M2;
+  constexpr bool kSplit = kQuantOut ? (MODE == MODE_PROMOTE && PATH == PATH_EXACT)
+                                    : (PATH == PATH_EXACT || MODE == MODE_MX4_PAIRS);
+  if constexpr (kSplit) {
+    const int64_t wave_cols = cus % ntm == 0 ? (cus / ntm) * 256 : 0;
+    const int64_t n1 = wave_cols > 0 ? (p.N / wave_cols) * wave_cols : 0, n2 = p.N - n1;
+    const int64_t last = kQuantOut ? ((p.M + 127) / 128) * ((n2 + 383) / 384) : ntm * ((n2 + 191) / 192);
+    if (big_tiles % cus != 0 && n1 > 0 && n2 > 0 && last <= cus) {
       const GemmArgs p1 = column_range(p, 0, n1, MODE, ODT), p2 = column_range(p, n1, n2, MODE, ODT);
       hipLaunchKernelGGL((k_gemm_tiled_256x256<AF, BF, MODE, ODT, PATH>), dim3((unsigned)(ntm * (n1 / 256))),
                          dim3(512), 0, st, p1);
-      if constexpr (ODT < ODT_Q_E4M3)
-        hipLaunchKernelGGL((k_gemm_tiled_256x192<AF, BF, MODE, ODT, PATH>),
-                           dim3((unsigned)(ntm * ((n2 + 191) / 192))), dim3(512), 0, st, p2);
+      if constexpr (kQuantOut)
+        hipLaunchKernelGGL((k_gemm_tiled_128x384<AF, BF, MODE, ODT, PATH>), dim3((unsigned)last), dim3(512), 0,
+                           st, p2);
+      else
+        hipLaunchKernelGGL((k_gemm_tiled_256x192<AF, BF, MODE, ODT, PATH>), dim3((unsigned)last), dim3(512), 0,
+                           st, p2);
       return;
     }
   }

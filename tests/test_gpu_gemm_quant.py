@@ -36,8 +36,11 @@ def _operands(M, N, K, xg, wg, seed):
 @pytest.mark.parametrize("xg,wg", [(T, T), (R, R), (TL, BL), (MX, MX)])
 @pytest.mark.parametrize("out_fmt", [fb.E4M3, fb.E5M2])
 def test_fused_quant_matches_quantized_fp32_result(xg, wg, out_fmt):
-    # (48, 256): 128x256 tiles with a ragged M; (4096, 4480): 256x256 tiles
-    for (M, N, K) in [(48, 256, 384), (272, 384, 640), (4096, 4480, 256)]:
+    # (48, 256): 128x256 tiles with a ragged M; (4096, 4480): 256x256 tiles,
+    # with exact promotion (TL, BL) its last 384 columns in 128x384 tiles;
+    # (4000, 7168): 256 + 256 tiles, the second wave 128x384 with a ragged M;
+    # (4096, 4608): a 128x384 tile with 128 valid columns
+    for (M, N, K) in [(48, 256, 384), (272, 384, 640), (4096, 4480, 256), (4000, 7168, 128), (4096, 4608, 128)]:
         xq, sx, wq, sw = _operands(M, N, K, xg, wg, seed=M + N + K + xg)
         a, sa, b, sb = dev(xq), dev(sx), dev(wq), dev(sw)
         for accum, rel in ACCUMS:
