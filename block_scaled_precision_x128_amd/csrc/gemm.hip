@@ -172,7 +172,8 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // assembly, in one descriptor per operand (a descriptor per block, kept live
   // through the multiply loop, costs scalar registers; offsets precomputed by
   // the compiler cost a vector register per load).  Offsets stay below
-  // 256 * K <= 2^30 bytes.
+  // 384 * K <= 1.5 * 2^30 bytes, and below 2^32 with the filler loads'
+  // kOutOfRange added (unsigned 32-bit offsets).
   const int q8 = lane >> 3;
   const int goff_even = q8 * (int)KB + (((lane & 7) ^ q8) << 4);
   const int goff_odd = q8 * (int)KB + (((lane & 7) ^ q8 ^ 1) << 4);
