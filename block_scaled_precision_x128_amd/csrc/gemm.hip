@@ -589,15 +589,21 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
     } else {
       // Exact path: four K=32 sub-steps on bf16 operands (MX scales folded in).
       v8bf xb[NJ][4];
+      u32x4 bd[NJ][2];   // MODE_PROMOTE: B's codes, converted among A tile 0's multiplies (below)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int r = b_row0 + 16 * j;
-        const float fsb = (MODE == MODE_MX) ? e8m0_to_f32((s_e[buf][0][TBM + r] >> (8 * g)) & 0xffu) : 1.0f;
         const u32x4 d0 = lds16(sb_, r * 128 + c0), d1 = lds16(sb_, r * 128 + c1);
-        xb[j][0] = cvt8<BF>(d0.x, d0.y, fsb);
-        xb[j][1] = cvt8<BF>(d0.z, d0.w, fsb);
-        xb[j][2] = cvt8<BF>(d1.x, d1.y, fsb);
-        xb[j][3] = cvt8<BF>(d1.z, d1.w, fsb);
+        if constexpr (MODE == MODE_PROMOTE) {
+          bd[j][0] = d0;
+          bd[j][1] = d1;
+        } else {
+          const float fsb = (MODE == MODE_MX) ? e8m0_to_f32((s_e[buf][0][TBM + r] >> (8 * g)) & 0xffu) : 1.0f;
+          xb[j][0] = cvt8<BF>(d0.x, d0.y, fsb);
+          xb[j][1] = cvt8<BF>(d0.z, d0.w, fsb);
+          xb[j][2] = cvt8<BF>(d1.x, d1.y, fsb);
+          xb[j][3] = cvt8<BF>(d1.z, d1.w, fsb);
+        }
       }
       if constexpr (MODE == MODE_PROMOTE) {
         // Software-pipelined order: A tile i+1 is read and converted while
@@ -631,11 +637,32 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
           __builtin_amdgcn_s_setprio(1);
           v4f pp[NJ];
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) pp[j] = mfma_bf16(xa[0], xb[j][0], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+          for (int s = 0; s < 4; ++s) {
+            // A tile 0 converts B's chunk s of every N tile just before the
+            // multiplies that use it, four conversions before each MFMA, so
+            // the matrix cores start 20 conversions into the step instead of
+            // 80 (both waves of a SIMD leave the barrier together and would
+            // otherwise convert at once): 2% faster at 4096x7168x7168 (A/B
+            // on one box, outputs bit-identical); A tile 0 converted the
+            // same way measured no better.
+            if (i == 0) {
 #pragma unroll
-          for (int s = 1; s < 4; ++s)
+              for (int j = 0; j < NJ; ++j) {
+                const u32x4 d = bd[j][s >> 1];
+                xb[j][s] = (s & 1) ? cvt8<BF>(d.z, d.w, 1.0f) : cvt8<BF>(d.x, d.y, 1.0f);
+              }
+            }
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) pp[j] = mfma_bf16(xa[s], xb[j][s], pp[j]);
+            for (int j = 0; j < NJ; ++j)
+              pp[j] = mfma_bf16(xa[s], xb[j][s], s == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : pp[j]);
+          }
+          if (i == 0) {
+#pragma unroll
+            for (int z = 0; z < 4 * NJ; ++z) {
+              __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            }
+          }
           __builtin_amdgcn_s_setprio(0);
           // lane: output rows 16 i + 4 g + q, column 16 j + l%16
 #pragma unroll
