@@ -1,7 +1,9 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times: quantize both operands bit-exactly against the oracle over
 the whole tensors, then check the GEMM on sampled output elements against the
-oracle's fp64 reference (in the workload's output dtype and in fp32)."""
+oracle's fp64 reference (in the workload's output dtype and in fp32), and the
+quantized-output GEMM's codes and scales on sampled rows against the oracle's
+quantization of the same kernel's fp32 result."""
 
 import numpy as np
 import pytest
@@ -11,7 +13,7 @@ import block_scaled_precision_x128_amd as fb
 import workloads
 from oracle import gemm
 from gpu_helpers import (NATIVE_REL_TOL, assert_codes_equal, assert_scales_equal, dev, full_operands, gemm_check,
-                         host, say)
+                         host, oracle_quantize, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,5 +58,24 @@ def test_full_size_workload(name):
         worst = gemm_check(got, odt, ref, absb, f"{name} algo={algo} accum={accum} odt={odt}", rel)
         say("worst error / bound", f"{worst:.3g}")
         del out, full
+
+    # The quantized-output GEMM at full size (the launch the benchmark times for
+    # the fused epilogue): codes and 1x128 scales of sampled rows, bit for bit,
+    # against the oracle's quantization of the same kernel's fp32 rows.
+    if wl.N % 128 == 0:
+        rows = um[:: max(1, len(um) // 64)]
+        for accum in (fb.ACCUM_FP32, fb.ACCUM_NATIVE):
+            say("gemm quantized output full size", name, "accum", accum, "rows", len(rows))
+            yf = fb.fp8_gemm_blockscaled(a, wl.x_fmt, wl.x_gran, sa, b, wl.w_fmt, wl.w_gran, sb, fb.DT_F32,
+                                         algo=fb.GEMM_TILED, accum=accum)
+            codes, scales = fb.fp8_gemm_blockscaled_quant(a, wl.x_fmt, wl.x_gran, sa, b, wl.w_fmt, wl.w_gran, sb,
+                                                          fb.E4M3, accum=accum)
+            torch.cuda.synchronize()
+            yh = host(yf)[rows]
+            want_q, want_s = oracle_quantize(yh, fb.GRAN_TILE_1x128, fb.E4M3)
+            label = f"{name} quantized output accum={accum}"
+            assert_scales_equal(host(scales)[rows], want_s, label)
+            assert_codes_equal(host(codes)[rows], want_q, label + " codes", yh)
+            del yf, codes, scales
     del a, b, sa, sb
     torch.cuda.empty_cache()
