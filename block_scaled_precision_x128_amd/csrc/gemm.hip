@@ -199,6 +199,11 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
   // This wave's row-block loads u0 .. u1-1 of step kb into stage buf (kb < 0:
   // loads past every descriptor, which read nothing and fill the stage with
   // zeros; a stage no step reads).
+  // The LDS address of stage 0 in a scalar register: each load's M0 is then
+  // formed by scalar adds (from a vector register it took a vector add and a
+  // readfirstlane per load, 16 vector instructions per step; 1.3% faster at
+  // 4096x7168x7168 on both paths, A/B on one box, outputs bit-identical).
+  const uint32_t smem_s = __builtin_amdgcn_readfirstlane(lds_addr(&smem[0][0]));
   auto issue_rows = [&](int kb, int buf, int u0, int u1) {
     const int kk = kb < 0 ? kOutOfRange : kb * 128;
 #pragma unroll
@@ -207,7 +212,7 @@ __device__ __forceinline__ void gemm_tiled_body(const GemmArgs& p) {
       const bool is_a = 8 * x < TBM;   // wave-uniform: scalar selects, no branch
       const int xl = is_a ? x : x - TBM / 8;
       const int goff = (x & 1) ? goff_odd : goff_even;
-      dma16_to_lds_add(is_a ? rs_a : rs_b, lds_addr(&smem[buf][8 * x * 128]), goff,
+      dma16_to_lds_add(is_a ? rs_a : rs_b, smem_s + (uint32_t)(buf * ((TBM + TBN) * TBK) + 8 * x * 128), goff,
                        __builtin_amdgcn_readfirstlane(off_add(xl * 8 * (int)KB, kk)));
     }
   };
