@@ -3,8 +3,10 @@ random shapes.  Half are drawn freely within the entry points' limits
 (M % 16, N % 128, K % 128); half sit where the tiled path changes its launch:
 grids of 256x256 tiles whose tile rows divide the CU count, with a column
 count that leaves a partial last wave, which the path splits off into
-narrower tiles (a ragged last tile row included).  So the tile classes and
-both kinds of column split are met at shapes that no other test names.
+narrower tiles (a ragged last tile row included); six more have M <= 64,
+where the automatic choice is the skinny kernel.  So the tile classes, both
+kinds of column split and the skinny kernel are met at shapes that no other
+test names.
 
 Each shape draws its scale pair, operand formats and output dtype; both
 accumulations run.  Sampled rows (first, last and random ones) are checked over
@@ -47,7 +49,14 @@ def _shapes(n: int, seed: int):
     return out
 
 
-SHAPES = _shapes(24, seed=20261203)
+def _skinny_shapes(n: int, seed: int):
+    # M <= 64: the automatic choice streams W through the skinny kernel
+    rng = np.random.default_rng(seed)
+    return [(16 * int(rng.integers(1, 5)), 128 * int(rng.integers(1, 160)), 128 * int(rng.integers(1, 17)))
+            for _ in range(n)]
+
+
+SHAPES = _shapes(24, seed=20261203) + _skinny_shapes(6, seed=20261204)
 
 
 @pytest.mark.parametrize("idx", range(len(SHAPES)))
